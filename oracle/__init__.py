@@ -1,0 +1,251 @@
+"""CPU oracle for single-pass MX quantization (bindings to ``liboracle.so``).
+
+TEST INFRASTRUCTURE ONLY: only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The GPU library never
+imports it and shares no code with it.
+
+The arithmetic lives in ``mx_oracle.c`` (plain C, binary64, nearest-value
+search for every rounding).  This module only marshals numpy arrays and, when
+asked, splits the rows of a matrix across threads; blocks never straddle a
+split, so the result does not depend on the thread count.
+
+Sources (web pages):
+  * pytorch/ao PR #4995 "[moe_training] Fused dual-axis MXFP8 quantization
+    with correct metadata" -- the dual-axis cast, its special values and the
+    uncovered-tail rule (PR description).
+  * AMD-AGI/ALTO PR #33 "feat: mx9: add fused MX9 quantization kernel with
+    pack/unpack" -- the MX9 storage format (Summary, Key design choices).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SOURCES = [os.path.join(_HERE, "mx_oracle.c")]
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"oracle library missing: {LIB_PATH} (run __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.oref_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oref_e4m3_value.restype = ctypes.c_double
+    lib.oref_e4m3_encode.argtypes = [ctypes.c_double]
+    lib.oref_e4m3_encode.restype = ctypes.c_uint8
+    lib.oref_rceil_byte.argtypes = [ctypes.c_double]
+    lib.oref_rceil_byte.restype = ctypes.c_int
+    for name in ("oref_mxfp8_rowwise", "oref_mxfp8_colwise"):
+        f = getattr(lib, name)
+        f.argtypes = [_P, _I64, _I64, _I64, _P, _P]
+        f.restype = None
+    lib.oref_mxfp8_dual.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P]
+    lib.oref_mxfp8_dual.restype = None
+    lib.oref_offs_check.argtypes = [_P, _I32, _I64]
+    lib.oref_offs_check.restype = ctypes.c_int
+    lib.oref_mxfp8_grouped.argtypes = [_P, _I64, _I64, _I64, _P, _I32, _P, _P, _P, _P]
+    lib.oref_mxfp8_grouped.restype = ctypes.c_int
+    lib.oref_mx9_pack.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P]
+    lib.oref_mx9_pack.restype = None
+    lib.oref_mx9_unpack.argtypes = [_P, _P, _P, _I64, _I64, ctypes.c_int, _P, _I64]
+    lib.oref_mx9_unpack.restype = None
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _splits(n: int, parts: int):
+    parts = max(1, min(parts, n))
+    edges = [n * k // parts for k in range(parts + 1)]
+    return [(edges[k], edges[k + 1]) for k in range(parts) if edges[k + 1] > edges[k]]
+
+
+def _run(jobs, threads: int):
+    if threads <= 1 or len(jobs) <= 1:
+        for j in jobs:
+            j()
+        return
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        for f in [ex.submit(j) for j in jobs]:
+            f.result()
+
+
+# --------------------------------------------------------------------------
+# scalar helpers (format definitions)
+# --------------------------------------------------------------------------
+
+def e4m3_value(code: int) -> float:
+    """Exact value of an OCP E4M3FN code (NaN for 0x7F / 0xFF)."""
+    return _load().oref_e4m3_value(code)
+
+
+def e4m3_encode(v: float) -> int:
+    """E4M3FN code nearest to v, ties to even, saturating at +-448."""
+    return _load().oref_e4m3_encode(float(v))
+
+
+def rceil_byte(amax: float) -> int:
+    """RCEIL E8M0 scale byte for a finite block maximum."""
+    return _load().oref_rceil_byte(float(amax))
+
+
+# --------------------------------------------------------------------------
+# MXFP8 dual-axis
+# --------------------------------------------------------------------------
+
+def _as_bf16_bits(x: np.ndarray) -> np.ndarray:
+    if x.dtype != np.uint16 or x.ndim != 2:
+        raise TypeError("expected a 2-D uint16 array of bf16 bit patterns")
+    if x.strides[1] != 2:
+        raise ValueError("rows must be contiguous")
+    return x
+
+
+def mxfp8_rowwise(x: np.ndarray, threads: int = 1):
+    """Rowwise 1x32 cast.  Returns (q_row [M,N] uint8, s_row [M,N/32] uint8)."""
+    x = _as_bf16_bits(x)
+    M, N = x.shape
+    assert N % 32 == 0
+    ld = x.strides[0] // 2
+    q = np.empty((M, N), np.uint8)
+    s = np.empty((M, N // 32), np.uint8)
+    lib = _load()
+
+    def job(r0, r1):
+        return lambda: lib.oref_mxfp8_rowwise(_ptr(x) + r0 * ld * 2, r1 - r0, N, ld,
+                                              _ptr(q) + r0 * N, _ptr(s) + r0 * (N // 32))
+    _run([job(a, b) for a, b in _splits(M, threads)], threads)
+    return q, s
+
+
+def mxfp8_colwise(x: np.ndarray, threads: int = 1):
+    """Colwise 32x1 cast.  Returns (q_col [N,M] uint8, s_col [M/32,N] uint8)."""
+    x = _as_bf16_bits(x)
+    M, N = x.shape
+    assert M % 32 == 0
+    ld = x.strides[0] // 2
+    q = np.empty((N, M), np.uint8)
+    s = np.empty((M // 32, N), np.uint8)
+    lib = _load()
+    slabs = [(32 * a, 32 * b) for a, b in _splits(M // 32, threads)]
+
+    def job(r0, r1):
+        def run():
+            qt = np.empty((N, r1 - r0), np.uint8)
+            lib.oref_mxfp8_colwise(_ptr(x) + r0 * ld * 2, r1 - r0, N, ld,
+                                   _ptr(qt), _ptr(s) + (r0 // 32) * N)
+            q[:, r0:r1] = qt
+        return run
+    _run([job(a, b) for a, b in slabs], threads)
+    return q, s
+
+
+def mxfp8_dual(x: np.ndarray, threads: int = 1):
+    """Fused dual-axis cast: (q_row, s_row, q_col, s_col)."""
+    q_row, s_row = mxfp8_rowwise(x, threads)
+    q_col, s_col = mxfp8_colwise(x, threads)
+    return q_row, s_row, q_col, s_col
+
+
+def offs_check(offs: np.ndarray, M: int) -> int:
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    return _load().oref_offs_check(_ptr(offs), len(offs), M)
+
+
+def mxfp8_grouped(x: np.ndarray, offs, threads: int = 1):
+    """Grouped cast.  Returns (code, outputs); outputs is None when the
+    offsets are invalid (code 1 order, 2 alignment, 3 bounds)."""
+    x = _as_bf16_bits(x)
+    M, N = x.shape
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    rc = offs_check(offs, M)
+    if rc != 0:
+        return rc, None
+    if threads <= 1:
+        q_row = np.empty((M, N), np.uint8)
+        s_row = np.empty((M, N // 32), np.uint8)
+        q_col = np.empty((N, M), np.uint8)
+        s_col = np.empty((M // 32, N), np.uint8)
+        rc = _load().oref_mxfp8_grouped(_ptr(x), M, N, x.strides[0] // 2, _ptr(offs), len(offs),
+                                        _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col))
+        return rc, (q_row, s_row, q_col, s_col)
+    # threaded: the dense cast by row slabs, then the tail rule of the C oracle
+    q_row, s_row, q_col, s_col = mxfp8_dual(x, threads)
+    covered = int(offs[-1]) if len(offs) else M
+    s_col[covered // 32:, :] = 0
+    return 0, (q_row, s_row, q_col, s_col)
+
+
+# --------------------------------------------------------------------------
+# MX9
+# --------------------------------------------------------------------------
+
+def mx9_pack(x: np.ndarray, threads: int = 1):
+    """Pack fp32 (given as float32 or uint32 bits) or bf16 (uint16 bits)
+    [rows, cols] along the last axis.  Returns (q [nb,16] int8,
+    max_exp [nb] uint8, prime [nb,1] uint8)."""
+    if x.ndim != 2 or x.strides[1] != x.itemsize:
+        raise ValueError("expected a 2-D array with contiguous rows")
+    if x.dtype in (np.float32, np.uint32):
+        dtype = 0
+    elif x.dtype == np.uint16:
+        dtype = 1
+    else:
+        raise TypeError("fp32 (float32/uint32) or bf16 (uint16 bits) only")
+    rows, cols = x.shape
+    ld = x.strides[0] // x.itemsize
+    nbr = (cols + 15) // 16
+    nb = rows * nbr
+    q = np.empty((nb, 16), np.int8)
+    e = np.empty(nb, np.uint8)
+    p = np.empty((nb, 1), np.uint8)
+    lib = _load()
+
+    def job(r0, r1):
+        return lambda: lib.oref_mx9_pack(_ptr(x) + r0 * ld * x.itemsize, dtype, r1 - r0, cols, ld,
+                                         _ptr(q) + r0 * nbr * 16, _ptr(e) + r0 * nbr,
+                                         _ptr(p) + r0 * nbr)
+    _run([job(a, b) for a, b in _splits(rows, threads)], threads)
+    return q, e, p
+
+
+def mx9_unpack(q: np.ndarray, max_exp: np.ndarray, prime: np.ndarray, rows: int, cols: int,
+               out_dtype: str = "fp32", threads: int = 1) -> np.ndarray:
+    """Unpack to [rows, cols]: float32 for "fp32", uint16 bf16 bits for "bf16"."""
+    nbr = (cols + 15) // 16
+    nb = rows * nbr
+    q = np.ascontiguousarray(q, dtype=np.int8).reshape(nb, 16)
+    max_exp = np.ascontiguousarray(max_exp, dtype=np.uint8).reshape(nb)
+    prime = np.ascontiguousarray(prime, dtype=np.uint8).reshape(nb)
+    if out_dtype == "fp32":
+        y = np.empty((rows, cols), np.float32)
+        od = 0
+    elif out_dtype == "bf16":
+        y = np.empty((rows, cols), np.uint16)
+        od = 1
+    else:
+        raise ValueError("out_dtype must be 'fp32' or 'bf16'")
+    lib = _load()
+
+    def job(r0, r1):
+        return lambda: lib.oref_mx9_unpack(_ptr(q) + r0 * nbr * 16, _ptr(max_exp) + r0 * nbr,
+                                           _ptr(prime) + r0 * nbr, r1 - r0, cols, od,
+                                           _ptr(y) + r0 * cols * y.itemsize, cols)
+    _run([job(a, b) for a, b in _splits(rows, threads)], threads)
+    return y

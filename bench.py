@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Benchmark of the single-pass MX quantization hot path on one MI355X.
+
+One step = the whole path over one batch: the fused dual-axis MXFP8 cast of a
+bf16 [32768, 8192] matrix (the stress workload: N(0,1) with subnormal and
+near-max tiles and Inf/NaN at rate 1e-6), then MX9 pack of the same matrix,
+then MX9 unpack back to bf16.  Inputs are resident in HBM before timing.
+
+Prints ONE JSON line.  ``value`` is the step's algorithmic bytes (what the
+method must read and write, per kernel) divided by the step time, in GB/s.
+``roofline`` describes the dominant kernel (the dual-axis cast): its
+algorithmic bytes per launch over its average launch time from HIP events on
+the launch stream, against MI355X's 8 TB/s HBM peak.  ``traffic`` is the HBM
+byte count per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+summary, reported only while the kernel source matches the source those
+counters were taken on.  ``cpu_baseline`` times the CPU oracle on a bounded
+sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--skip-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+M, N = 32768, 8192
+DUAL_BYTES_PER_ELEM = 2 + 1 + 1 + 1 / 32 + 1 / 32          # bf16 in; E4M3 x2 + E8M0 x2 out
+PACK_BF16_BYTES_PER_ELEM = 2 + 1 + 1 / 16 + 1 / 16         # bf16 in; q + max_exp + prime out
+UNPACK_BF16_BYTES_PER_ELEM = 1 + 1 / 16 + 1 / 16 + 2       # q + max_exp + prime in; bf16 out
+KERNEL_SOURCES = ["mx9_dual_axis_amd/csrc/dual_axis.hip"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "dual_axis_stress_counters.txt")
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per dual-axis launch from the committed counter summary, or
+    None when absent or taken on a different kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    txt = open(COUNTERS_FILE).read()
+    m_src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_src or not m_b or m_src.group(1) != source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(xb, threads: int, rows: int):
+    """The oracle, as it stands, on the first `rows` rows of the workload:
+    dual-axis cast + MX9 pack + MX9 unpack (bf16)."""
+    import oracle
+    sample = xb[:rows]
+    t0 = time.perf_counter()
+    oracle.mxfp8_dual(sample, threads=threads)
+    q, e, p = oracle.mx9_pack(sample, threads=threads)
+    oracle.mx9_unpack(q, e, p, rows, N, "bf16", threads=threads)
+    dt = time.perf_counter() - t0
+    nbytes = rows * N * (DUAL_BYTES_PER_ELEM + PACK_BF16_BYTES_PER_ELEM + UNPACK_BF16_BYTES_PER_ELEM)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} of {M} rows ({rows * N} elements) of the stress workload, "
+                      f"dual-axis cast + MX9 pack + unpack, {dt:.1f} s wall on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the method needs no exchange between GPUs; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mx9_dual_axis_amd as mxq
+    from mx9_dual_axis_amd import synth
+
+    dev = torch.device("cuda:0")
+    print("bench: generating the stress workload bf16 [32768, 8192] (seed 5)", file=sys.stderr, flush=True)
+    xb = synth.stress(M, N, 5)
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    dual_out = (torch.empty((M, N), **u8), torch.empty((M, N // 32), **u8),
+                torch.empty((N, M), **u8), torch.empty((M // 32, N), **u8))
+    nb = M * N // 16
+    mx9_out = (torch.empty((nb, 16), dtype=torch.int8, device=dev), torch.empty((nb,), **u8),
+               torch.empty((nb, 1), **u8))
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        mxq.mx_quantize_2d_dual(x, out=dual_out)
+        if ev: ev[1].record()
+        mxq.mx9_pack(x, out=mx9_out)
+        if ev: ev[2].record()
+        mxq.mx9_unpack(*mx9_out, M, N, out=y)
+        if ev: ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, bracketed by synchronizations
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_kernel = {"dual_axis": [], "mx9_pack": [], "mx9_unpack": []}
+    for ev in evs:
+        per_kernel["dual_axis"].append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        per_kernel["mx9_pack"].append(ev[1].elapsed_time(ev[2]) * 1e-3)
+        per_kernel["mx9_unpack"].append(ev[2].elapsed_time(ev[3]) * 1e-3)
+    elems = M * N
+    kbytes = {"dual_axis": elems * DUAL_BYTES_PER_ELEM, "mx9_pack": elems * PACK_BF16_BYTES_PER_ELEM,
+              "mx9_unpack": elems * UNPACK_BF16_BYTES_PER_ELEM}
+    kernels = {}
+    for k, ts in per_kernel.items():
+        t = sum(ts) / len(ts)
+        kernels[k] = {"us": round(t * 1e6, 2), "bytes": int(kbytes[k]), "GB_s": round(kbytes[k] / t / 1e9, 1),
+                      "frac": round(kbytes[k] / t / 1e9 / PEAK_HBM_GBS, 4)}
+    step_bytes = sum(kbytes.values())
+    ms_per_step = wall / args.steps * 1e3
+    value = step_bytes / (wall / args.steps) / 1e9
+
+    # context: a device-to-device copy of one dual-axis launch's byte volume
+    half = int(kbytes["dual_axis"] // 2)
+    src = torch.empty(half, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * half * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
+    dual = kernels["dual_axis"]
+    line = {
+        "metric": "achieved HBM GB/s (fraction of MI355X peak) for dual-axis MXFP8 + MX9",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded stress workload: N(0,1), 0.5% subnormal tiles, 0.5% near-max tiles, Inf/NaN 1e-6)",
+        "config": {"workload": "stress bf16 [32768, 8192]: dual-axis MXFP8 cast + MX9 pack + MX9 unpack to bf16",
+                   "M": M, "N": N, "block_mxfp8": 32, "block_mx9": 16, "scaling_mode": "rceil",
+                   "step_algorithmic_bytes": int(step_bytes)},
+        "roofline": {"bound": "hbm", "achieved": dual["GB_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(dual["GB_s"] / PEAK_HBM_GBS, 4), "traffic": committed_traffic(),
+                     "kernel": "dual_axis_kernel<false>", "algorithmic_bytes_per_launch": dual["bytes"],
+                     "avg_launch_us": dual["us"]},
+        "kernels": kernels,
+        "copy_GB_s": round(copy_gbs, 1),
+        "kernel_source_sha256_16": source_digest(),
+    }
+    if not args.skip_cpu:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        print(f"bench: timing the CPU oracle on {args.cpu_rows} rows, {threads} threads", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(xb, threads, args.cpu_rows)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+/*
+ * mxq.h -- C ABI of libmxq.so: single-pass block-scaled (MX) quantization
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages):
+ *   [MXFP8] pytorch/ao PR #4995, "[moe_training] Fused dual-axis MXFP8
+ *           quantization with correct metadata".
+ *   [MX9]   AMD-AGI/ALTO PR #33, "feat: mx9: add fused MX9 quantization
+ *           kernel with pack/unpack".
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named x, q*, s*, offs, err, y, max_exp and prime are DEVICE
+ *     pointers.  The caller allocates and owns every buffer; the library
+ *     allocates nothing, keeps no state between calls and never waits on the
+ *     device.
+ *   - stream is a hipStream_t passed as void*; NULL means the default stream.
+ *     All work is enqueued on that stream only, so a call may be captured in a
+ *     HIP graph.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     nonzero return (an mx_status) therefore means nothing was launched and
+ *     no output byte was written; MX_E_LAUNCH reports a failed launch.
+ *   - Buffers of an empty call (a zero dimension) may be NULL.
+ *   - Byte intervals of all buffers passed to one call must be pairwise
+ *     disjoint (MX_E_OVERLAP).  Sizes are in elements unless stated.
+ *   - Calls on different streams that share an output buffer race.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mx_status {
+    MX_OK = 0,
+    MX_E_NULL = 1,      /* a required pointer is NULL                        */
+    MX_E_DTYPE = 2,     /* unsupported element type (fp16 and others)        */
+    MX_E_BLOCK = 3,     /* block_size is not the format's (32 MXFP8, 16 MX9)  */
+    MX_E_MODE = 4,      /* scaling_mode other than RCEIL                     */
+    MX_E_SHAPE = 5,     /* dimensions negative, too large, or not multiples   */
+    MX_E_STRIDE = 6,    /* row pitch smaller than the row or misaligned       */
+    MX_E_ALIGN = 7,     /* pointer alignment                                  */
+    MX_E_OVERLAP = 8,   /* two buffers of one call overlap                    */
+    MX_E_LAUNCH = 9     /* the HIP launch failed                              */
+} mx_status;
+
+enum { MX_DTYPE_F32 = 0, MX_DTYPE_BF16 = 1 };
+enum { MX_SCALE_RCEIL = 0 };
+
+/* Codes the grouped cast writes to *err (device side). */
+enum { MX_OFFS_OK = 0, MX_OFFS_ORDER = 1, MX_OFFS_ALIGN = 2, MX_OFFS_BOUNDS = 3 };
+
+/*
+ * mx_quantize_2d_dual -- fused dual-axis MXFP8 cast ([MXFP8], PR
+ * description: one read of the bf16 input, four outputs; the
+ * "Bug-compatible" list and the NaN paragraph fix the special values).
+ *
+ *   x      bf16 bit patterns, [M, N] row-major with row pitch ld_x elements.
+ *   q_row  uint8 E4M3FN codes [M, N] (pitch N): rowwise 1x32 blocks.
+ *   s_row  uint8 E8M0 scales  [M, N/32] (pitch N/32).
+ *   q_col  uint8 E4M3FN codes [N, M] (pitch M): colwise 32x1 blocks, stored
+ *          transposed, so q_col[n][m] encodes x[m][n].
+ *   s_col  uint8 E8M0 scales  [M/32, N] (pitch N).
+ *   block_size must be 32, scaling_mode MX_SCALE_RCEIL.
+ *
+ * Per block: RCEIL scale byte b (smallest power of two that brings the block
+ * maximum to <= 448, byte 0 for an all-zero block); element = E4M3FN of
+ * x * 2^(127-b), nearest-even.  NaN in a block: scale 255, every code 0x7F,
+ * on both axes.  Inf (no NaN): rowwise scale 255 with 0x7F codes; colwise
+ * scale 254 with +-Inf -> +-448 and the other elements scaled by 2^-127.
+ *
+ * Errors: MX_E_NULL (a pointer NULL while M, N > 0), MX_E_BLOCK, MX_E_MODE, MX_E_SHAPE
+ * (M or N negative, not a multiple of 128, or above 2^30), MX_E_STRIDE
+ * (ld_x < N or ld_x not a multiple of 8), MX_E_ALIGN (any pointer not
+ * 16-byte aligned), MX_E_OVERLAP.  M == 0 or N == 0 is a no-op.
+ */
+int mx_quantize_2d_dual(const uint16_t *x, int64_t M, int64_t N, int64_t ld_x,
+                        int32_t block_size, int32_t scaling_mode,
+                        uint8_t *q_row, uint8_t *s_row,
+                        uint8_t *q_col, uint8_t *s_col, void *stream);
+
+/*
+ * mx_quantize_grouped -- the dual-axis cast of a MoE activation buffer
+ * whose rows are split into G groups by cumulative ends offs[0..G-1]
+ * ([MXFP8], PR description, "Uncovered tail" paragraph; review reply on
+ * offset validation).
+ *
+ * Outputs are exactly those of mx_quantize_2d_dual on the whole buffer,
+ * except that s_col rows i >= offs[G-1]/32 (the uncovered tail) are zero.
+ * Tail rows are still quantized on both axes; empty groups change nothing.
+ * G == 0 is the dense cast (offs may then be NULL).
+ *
+ *   offs  int32 device array [G]; valid when 0 <= offs[0] <= ... <=
+ *         offs[G-1] <= M and every entry is a multiple of 128.
+ *   err   int32 device word or NULL.  When non-NULL the call writes
+ *         MX_OFFS_OK, or the code of the first invalid entry (bounds are
+ *         checked before alignment, alignment before order).  With invalid
+ *         offsets the outputs are unspecified, but nothing outside the four
+ *         output buffers and *err is written.
+ *
+ * Host-side errors as for mx_quantize_2d_dual, plus MX_E_SHAPE for G < 0
+ * and MX_E_NULL for G > 0 with offs == NULL; offs and err take part in the
+ * overlap check.
+ */
+int mx_quantize_grouped(const uint16_t *x, int64_t M, int64_t N, int64_t ld_x,
+                        int32_t block_size, int32_t scaling_mode,
+                        const int32_t *offs, int32_t G,
+                        uint8_t *q_row, uint8_t *s_row,
+                        uint8_t *q_col, uint8_t *s_col,
+                        int32_t *err, void *stream);
+
+/*
+ * mx9_pack -- MX9 pack along the last axis, block 16 ([MX9], Summary and
+ * Key design choices).
+ *
+ *   x        fp32 (dtype MX_DTYPE_F32) or bf16 (MX_DTYPE_BF16) bit patterns,
+ *            [rows, cols] row-major, row pitch ld_x elements.
+ *   q        int8 [nb, 16], nb = rows * ceil(cols/16), blocks numbered
+ *            row-major over (row, block within the row).
+ *   max_exp  uint8 [nb]: shared exponent as E8M0 (true exponent + 127), the
+ *            true exponent taken from the input's own exponent field and
+ *            raised to at least -126, so the byte is in [1, 254] for
+ *            finite input.
+ *   prime    uint8 [nb]: bit j (LSB first) set when pair j (elements 2j,
+ *            2j+1) lies wholly below 2^E and is quantized on the finer grid.
+ *   q = round-half-even(x / 2^(E - 6 - p)) clamped to [-127, 127].  A block
+ *   holding Inf or NaN gets max_exp 255, q 0 and prime 0.  A trailing
+ *   partial block is padded with +0.
+ *
+ * Errors: MX_E_NULL, MX_E_DTYPE (dtype not F32/BF16), MX_E_BLOCK
+ * (block_size != 16), MX_E_SHAPE (negative or too large), MX_E_STRIDE
+ * (ld_x < cols), MX_E_ALIGN (x not aligned to its element size, q not
+ * 16-byte aligned), MX_E_OVERLAP.  rows == 0 or cols == 0 is a no-op.
+ */
+int mx9_pack(const void *x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld_x,
+             int32_t block_size, int8_t *q, uint8_t *max_exp, uint8_t *prime,
+             void *stream);
+
+/*
+ * mx9_unpack -- inverse of mx9_pack ([MX9], convert_from_mx9; the caller
+ * passes the shape back because it is not stored).
+ *
+ *   y = q * 2^(max_exp - 127 - 6 - p) for max_exp != 255, written as fp32
+ *   (out_dtype MX_DTYPE_F32; exact, IEEE overflow to Inf for the one
+ *   combination q = -128, max_exp = 254, p = 0 that pack never emits) or
+ *   bf16 (MX_DTYPE_BF16; nearest-even, exact for everything pack emits).
+ *   max_exp == 255 gives the quiet NaN 0x7FC00000 / 0x7FC0.
+ *   y is [rows, cols] with row pitch ld_y elements; only the first cols
+ *   columns of each row are written.
+ *
+ * Errors: MX_E_NULL, MX_E_DTYPE, MX_E_BLOCK, MX_E_SHAPE, MX_E_STRIDE
+ * (ld_y < cols), MX_E_ALIGN (q not 16-byte aligned, y not aligned to its
+ * element size), MX_E_OVERLAP.  rows == 0 or cols == 0 is a no-op.
+ */
+int mx9_unpack(const int8_t *q, const uint8_t *max_exp, const uint8_t *prime,
+               int64_t rows, int64_t cols, int32_t block_size, int32_t out_dtype,
+               void *y, int64_t ld_y, void *stream);
+
+/* Host function: a static, human-readable name for an mx_status value. */
+const char *mx_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

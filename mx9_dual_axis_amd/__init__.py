@@ -1,1 +1,225 @@
-"""placeholder; replaced by the binding"""
+"""Single-pass MX quantization on AMD Instinct MI355X (gfx950).
+
+Python binding over ``libmxq.so`` (C ABI in ``include/mxq.h``).  The binding
+only marshals arguments: it allocates output tensors with torch, passes raw
+device pointers, sizes and the current HIP stream, and raises on a nonzero
+status.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback, and a missing library raises immediately.
+
+Entry points (same names as the C ABI):
+  mx_quantize_2d_dual(x)                 -> (q_row, s_row, q_col, s_col)
+  mx_quantize_grouped(x, offs, err=None) -> (q_row, s_row, q_col, s_col)
+  mx9_pack(x)                            -> (q, max_exp, prime)
+  mx9_unpack(q, max_exp, prime, rows, cols, out_dtype) -> y
+plus the signatures the pages use: ``mxfp8_quantize_2d_1x32_32x1`` (dense
+when ``offs`` is None, grouped otherwise), ``convert_to_mx9`` and
+``convert_from_mx9``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxq.so")
+
+MX_DTYPE_F32 = 0
+MX_DTYPE_BF16 = 1
+MX_SCALE_RCEIL = 0
+OFFS_CODES = {0: "ok", 1: "offsets not ascending", 2: "offset not a multiple of 128",
+              3: "offset outside [0, M]"}
+
+_lib = None
+
+
+class MXError(ValueError):
+    """A nonzero mx_status returned by the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing (run __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.mx_quantize_2d_dual.argtypes = [P, I64, I64, I64, I32, I32, P, P, P, P, P]
+    lib.mx_quantize_grouped.argtypes = [P, I64, I64, I64, I32, I32, P, I32, P, P, P, P, P, P]
+    lib.mx9_pack.argtypes = [P, I32, I64, I64, I64, I32, P, P, P, P]
+    lib.mx9_unpack.argtypes = [P, P, P, I64, I64, I32, I32, P, I64, P]
+    for f in (lib.mx_quantize_2d_dual, lib.mx_quantize_grouped, lib.mx9_pack, lib.mx9_unpack):
+        f.restype = ctypes.c_int
+    lib.mx_status_string.argtypes = [ctypes.c_int]
+    lib.mx_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes library (raises if it has not been built)."""
+    return _load()
+
+
+def status_string(status: int) -> str:
+    return _load().mx_status_string(status).decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise MXError(rc, status_string(rc))
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need_cuda(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _scaling(mode) -> int:
+    if mode in ("rceil", MX_SCALE_RCEIL):
+        return MX_SCALE_RCEIL
+    return -1  # rejected by the library with MX_E_MODE
+
+
+def _dual_outputs(x: torch.Tensor, out):
+    M, N = x.shape
+    if out is not None:
+        return out
+    kw = dict(dtype=torch.uint8, device=x.device)
+    return (torch.empty((M, N), **kw), torch.empty((M, N // 32), **kw),
+            torch.empty((N, M), **kw), torch.empty((M // 32, N), **kw))
+
+
+def _bf16_matrix(x: torch.Tensor):
+    _need_cuda(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise MXError(2, status_string(2))
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with contiguous rows")
+
+
+def mx_quantize_2d_dual(x: torch.Tensor, block_size: int = 32, scaling_mode="rceil", out=None):
+    """Fused dual-axis MXFP8 cast.  Returns uint8 tensors q_row [M,N] (E4M3),
+    s_row [M,N/32] (E8M0), q_col [N,M] (E4M3, transposed), s_col [M/32,N]."""
+    _bf16_matrix(x)
+    M, N = x.shape
+    q_row, s_row, q_col, s_col = _dual_outputs(x, out)
+    _check(_load().mx_quantize_2d_dual(x.data_ptr(), M, N, x.stride(0), block_size, _scaling(scaling_mode),
+                                       q_row.data_ptr(), s_row.data_ptr(), q_col.data_ptr(),
+                                       s_col.data_ptr(), _stream(x.device)))
+    return q_row, s_row, q_col, s_col
+
+
+def mx_quantize_grouped(x: torch.Tensor, offs: torch.Tensor, block_size: int = 32, scaling_mode="rceil",
+                        err: torch.Tensor | None = None, out=None):
+    """Grouped dual-axis cast: the dense outputs, with the colwise scale rows
+    of the uncovered tail (rows >= offs[-1]) zeroed.  ``err`` (int32 device
+    tensor of one element) receives the device-side offset check code."""
+    _bf16_matrix(x)
+    M, N = x.shape
+    if offs.dtype != torch.int32 or offs.dim() != 1 or not offs.is_contiguous():
+        raise ValueError("offs must be a contiguous 1-D int32 tensor")
+    _need_cuda(offs, "offs")
+    if err is not None:
+        _need_cuda(err, "err")
+        if err.dtype != torch.int32 or err.numel() != 1:
+            raise ValueError("err must be a one-element int32 tensor")
+    q_row, s_row, q_col, s_col = _dual_outputs(x, out)
+    _check(_load().mx_quantize_grouped(x.data_ptr(), M, N, x.stride(0), block_size, _scaling(scaling_mode),
+                                       offs.data_ptr() if offs.numel() else None, offs.numel(),
+                                       q_row.data_ptr(), s_row.data_ptr(), q_col.data_ptr(),
+                                       s_col.data_ptr(), _ptr(err), _stream(x.device)))
+    return q_row, s_row, q_col, s_col
+
+
+def _mx9_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MX_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return MX_DTYPE_BF16
+    return 2  # any other dtype: the library answers MX_E_DTYPE
+
+
+def mx9_pack(x: torch.Tensor, block_size: int = 16, out=None):
+    """MX9 pack along the last axis.  Returns q int8 [nb,16], max_exp uint8
+    [nb], prime uint8 [nb,1], nb = rows * ceil(cols/16).  x is fp32 or bf16,
+    2-D with contiguous rows (a 1-D tensor is one row)."""
+    _need_cuda(x, "x")
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with contiguous rows")
+    rows, cols = x.shape
+    nb = rows * ((cols + 15) // 16)
+    if out is None:
+        q = torch.empty((nb, 16), dtype=torch.int8, device=x.device)
+        e = torch.empty((nb,), dtype=torch.uint8, device=x.device)
+        p = torch.empty((nb, 1), dtype=torch.uint8, device=x.device)
+    else:
+        q, e, p = out
+    _check(_load().mx9_pack(x.data_ptr(), _mx9_dtype(x), rows, cols, x.stride(0), block_size,
+                            q.data_ptr(), e.data_ptr(), p.data_ptr(), _stream(x.device)))
+    return q, e, p
+
+
+def mx9_unpack(q: torch.Tensor, max_exp: torch.Tensor, prime: torch.Tensor, rows: int, cols: int,
+               out_dtype=torch.float32, block_size: int = 16, out: torch.Tensor | None = None):
+    """MX9 unpack to [rows, cols] of out_dtype (float32 or bfloat16)."""
+    for t, n in ((q, "q"), (max_exp, "max_exp"), (prime, "prime")):
+        _need_cuda(t, n)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    if q.dtype != torch.int8 or max_exp.dtype != torch.uint8 or prime.dtype != torch.uint8:
+        raise ValueError("q must be int8, max_exp and prime uint8")
+    nb = rows * ((cols + 15) // 16)
+    if q.numel() != nb * 16 or max_exp.numel() != nb or prime.numel() != nb:
+        raise ValueError("q / max_exp / prime sizes do not match rows and cols")
+    if out is not None:
+        out_dtype = out.dtype
+    od = {torch.float32: MX_DTYPE_F32, torch.bfloat16: MX_DTYPE_BF16}.get(out_dtype, 2)
+    if out is None:
+        y = torch.empty((rows, cols), dtype=out_dtype if od != 2 else torch.float32, device=q.device)
+    else:
+        y = out
+        if y.dim() != 2 or y.stride(1) != 1 or y.shape[0] != rows or y.shape[1] < cols:
+            raise ValueError("out must be [rows, >= cols] with contiguous rows")
+    _check(_load().mx9_unpack(q.data_ptr(), max_exp.data_ptr(), prime.data_ptr(), rows, cols,
+                              block_size, od, y.data_ptr(), y.stride(0), _stream(q.device)))
+    return y
+
+
+# --- the pages' call signatures ------------------------------------------
+
+def mxfp8_quantize_2d_1x32_32x1(x: torch.Tensor, block_size: int = 32, scaling_mode="rceil",
+                                offs: torch.Tensor | None = None):
+    """Dense cast when offs is None, grouped cast otherwise."""
+    if offs is None:
+        return mx_quantize_2d_dual(x, block_size, scaling_mode)
+    return mx_quantize_grouped(x, offs, block_size, scaling_mode)
+
+
+def convert_to_mx9(x: torch.Tensor, block_size: int = 16):
+    return mx9_pack(x.reshape(-1, x.shape[-1]), block_size)
+
+
+def convert_from_mx9(q, max_exp, prime, out_dtype, shape, block_size: int = 16):
+    shape = tuple(shape)
+    cols = shape[-1]
+    rows = 1
+    for s in shape[:-1]:
+        rows *= s
+    return mx9_unpack(q, max_exp, prime, rows, cols, out_dtype, block_size).reshape(shape)

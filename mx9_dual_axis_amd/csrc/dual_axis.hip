@@ -1,0 +1,245 @@
+// dual_axis.hip -- fused dual-axis MXFP8 cast for gfx950 (CDNA4).
+//
+// Operation: pytorch/ao PR #4995, "[moe_training] Fused dual-axis MXFP8
+// quantization with correct metadata" (PR description).  One read of a bf16
+// matrix produces rowwise 1x32 and colwise 32x1 E4M3 data with E8M0 RCEIL
+// scales; colwise data is stored transposed.
+//
+// Work decomposition: one workgroup (4 wave64s) per 128x128 tile.
+//   * load   : each thread holds eight 16-byte row segments (8 bf16 each); a
+//              wave's load instruction covers four full 256-byte tile rows.
+//   * rowwise: a 1x32 block is four adjacent lanes; the block maximum is a
+//              packed u16 max of the sign-masked bf16 patterns followed by a
+//              two-step DPP quad reduction.  Masking the sign makes the
+//              integer order NaN > Inf > finite, so the special cases need no
+//              per-element test.
+//   * LDS    : the tile is written once (32 KiB) for the colwise pass.
+//   * colwise: each thread owns a column pair and one 32-row block: 32 LDS
+//              dwords, a packed u16 max gives both column maxima at once;
+//              v_perm regroups (row m, row m+1) pairs of one column so the
+//              packed scaled cast yields m-contiguous bytes, stored as two
+//              16-byte writes per column of the transposed output.
+//   * cast   : v_cvt_scalef32_pk_fp8_bf16 divides by the E8M0 scale 2^(b-127)
+//              given as fp32 bits b<<23 (byte 0 acts as 2^-127, i.e. the 2^127
+//              multiplier) and rounds to nearest even; it does not saturate,
+//              so the colwise Inf block (scale 254) maps its NaN bytes to
+//              +-448 afterwards, and poisoned blocks are overwritten with 0x7F.
+//   * order  : workgroups are dispatched round-robin over the 8 XCDs; each XCD
+//              is given a contiguous range of tiles so that the tiles sharing
+//              an s_row cache line are written through the same L2.
+#include "mxq_kernels.h"
+
+#include <limits.h>
+
+namespace mxq {
+namespace {
+
+constexpr int kTile = 128;
+constexpr int kThreads = 256;
+constexpr uint32_t kXcds = 8;
+
+typedef short v2i16 __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+
+// RCEIL scale byte from the largest sign-masked finite bf16 pattern a of a
+// block.  448 = 1.75 * 2^8, so ceil(log2(A / 448)) = (e - 135) + [1.m > 1.75]
+// for a normal A with exponent field e and fraction m; biased by 127 and
+// clamped below at 0 (zero and tiny blocks).  Largest finite result: 247.
+__device__ __forceinline__ uint32_t rceil_byte(uint32_t a) {
+    const int b = int(a >> 7) - 8 + ((a & 0x7Fu) > 0x60u ? 1 : 0);
+    return b > 0 ? uint32_t(b) : 0u;
+}
+
+// Rowwise scale: the 1x32 cast converts without saturation, so Inf as well
+// as NaN makes the whole block NaN with scale 255.
+__device__ __forceinline__ uint32_t row_scale(uint32_t a) {
+    return a >= 0x7F80u ? 255u : rceil_byte(a);
+}
+
+// Colwise scale: NaN poisons (255); Inf without NaN saturates (254).
+__device__ __forceinline__ uint32_t col_scale(uint32_t a) {
+    return a > 0x7F80u ? 255u : (a == 0x7F80u ? 254u : rceil_byte(a));
+}
+
+// E8M0 byte as the fp32 scale operand of the scaled conversion.
+__device__ __forceinline__ float e8m0_operand(uint32_t b) {
+    return __uint_as_float((b < 254u ? b : 254u) << 23);
+}
+
+// Four bf16 (two packed pairs, in order) -> four E4M3 bytes, x / 2^(b-127).
+__device__ __forceinline__ uint32_t cvt4(uint32_t pair01, uint32_t pair23, float scale) {
+    v2i16 r = {0, 0};
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(v2bf16, pair01), scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(v2bf16, pair23), scale, true);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// In a colwise Inf block the only NaN bytes (0x7F / 0xFF) come from +-Inf;
+// satfinite turns them into +-448 (0x7E / 0xFE).  Adding 1 to the low seven
+// bits carries into bit 7 exactly for those bytes.
+__device__ __forceinline__ uint32_t nan_bytes_to_max(uint32_t w) {
+    const uint32_t t = (w & 0x7F7F7F7Fu) + 0x01010101u;
+    return w - ((t & 0x80808080u) >> 7);
+}
+
+// Offset validation code of group g: bounds, then alignment, then order.
+__device__ __forceinline__ int32_t offs_code(const int32_t* offs, int32_t g, int64_t M) {
+    const int32_t o = offs[g];
+    if (o < 0 || int64_t(o) > M) return 3;
+    if (o % 128 != 0) return 2;
+    if (g > 0 && o < offs[g - 1]) return 1;
+    return 0;
+}
+
+// Whole workgroup: first invalid group's code (0 if none) into *err.
+__device__ void validate_offsets(const int32_t* offs, int32_t G, int64_t M, int32_t* err) {
+    __shared__ int32_t first_bad;
+    if (threadIdx.x == 0) first_bad = INT_MAX;
+    __syncthreads();
+    for (int32_t g = threadIdx.x; g < G; g += kThreads)
+        if (offs_code(offs, g, M) != 0) atomicMin(&first_bad, g);
+    __syncthreads();
+    if (threadIdx.x == 0) *err = first_bad == INT_MAX ? 0 : offs_code(offs, first_bad, M);
+}
+
+template <bool kGrouped>
+__global__ __launch_bounds__(kThreads)
+void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, int64_t N,
+                      uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
+                      uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
+                      uint32_t tiles_n, uint32_t tiles,
+                      const int32_t* __restrict__ offs, int32_t G, int32_t* __restrict__ err) {
+    __shared__ uint4 lds_tile[kTile * 16];     // [128 rows][16 x 16 bytes]
+    __shared__ uint32_t lds_srow[kTile];       // the tile's 4 rowwise scale bytes per row
+
+    const uint32_t t = threadIdx.x;
+    const uint32_t bid = blockIdx.x;
+    const uint32_t per = tiles / kXcds, rem = tiles % kXcds;
+    const uint32_t xcd = bid % kXcds, loc = bid / kXcds;
+    const uint32_t tile = xcd * per + min(xcd, rem) + loc;
+    const int64_t m0 = int64_t(tile / tiles_n) * kTile;
+    const int64_t n0 = int64_t(tile % tiles_n) * kTile;
+
+    // first block row of the uncovered tail (grouped only)
+    int64_t tail_br = M / 32;
+    if (kGrouped) {
+        if (G > 0) {
+            int64_t last = offs[G - 1];
+            last = last < 0 ? 0 : (last > M ? M : last);
+            tail_br = last / 32;
+        }
+        if (err != nullptr && bid == 0) validate_offsets(offs, G, M, err);
+    }
+
+    // ---- load the tile: rows 16k + rsub, columns c8 .. c8+7 ----
+    const uint32_t rsub = t >> 4;
+    const uint32_t c8 = (t & 15u) * 8u;
+    const uint16_t* xt = x + m0 * ld_x + n0 + c8;
+    uint4 d[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        d[k] = *reinterpret_cast<const uint4*>(xt + int64_t(16 * k + rsub) * ld_x);
+
+    // ---- rowwise 1x32 pass ----
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t r = 16u * k + rsub;
+        lds_tile[r * 16u + (t & 15u)] = d[k];
+        const uint32_t mx = pk_max_u16(pk_max_u16(d[k].x & 0x7FFF7FFFu, d[k].y & 0x7FFF7FFFu),
+                                       pk_max_u16(d[k].z & 0x7FFF7FFFu, d[k].w & 0x7FFF7FFFu));
+        uint32_t a = max(mx & 0xFFFFu, mx >> 16);
+        a = max(a, uint32_t(__builtin_amdgcn_mov_dpp(int(a), 0xB1, 0xF, 0xF, true)));  // lane ^ 1
+        a = max(a, uint32_t(__builtin_amdgcn_mov_dpp(int(a), 0x4E, 0xF, 0xF, true)));  // lane ^ 2
+        const uint32_t b = row_scale(a);
+        const float sc = e8m0_operand(b);
+        uint2 o;
+        o.x = cvt4(d[k].x, d[k].y, sc);
+        o.y = cvt4(d[k].z, d[k].w, sc);
+        if (b == 255u) o = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+        *reinterpret_cast<uint2*>(q_row + (m0 + r) * N + n0 + c8) = o;
+        if ((t & 3u) == 0u) reinterpret_cast<uint8_t*>(lds_srow)[r * 4u + ((t & 15u) >> 2)] = uint8_t(b);
+    }
+    __syncthreads();
+
+    if (t < kTile)
+        *reinterpret_cast<uint32_t*>(s_row + (m0 + t) * (N / 32) + n0 / 32) = lds_srow[t];
+
+    // ---- colwise 32x1 pass: columns 2cp, 2cp+1 of rows 32br .. 32br+31 ----
+    const uint32_t cp = t & 63u;
+    const uint32_t br = t >> 6;
+    const uint32_t* lt = reinterpret_cast<const uint32_t*>(lds_tile);
+    uint32_t v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = lt[(32u * br + i) * 64u + cp];
+    uint32_t cm = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) cm = pk_max_u16(cm, v[i] & 0x7FFF7FFFu);
+    const uint32_t b_lo = col_scale(cm & 0xFFFFu);
+    const uint32_t b_hi = col_scale(cm >> 16);
+    const float s_lo = e8m0_operand(b_lo), s_hi = e8m0_operand(b_hi);
+    uint32_t w_lo[8], w_hi[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        // (row 4u, row 4u+1) and (row 4u+2, row 4u+3) of each column
+        const uint32_t lo01 = __builtin_amdgcn_perm(v[4 * u + 1], v[4 * u], 0x05040100u);
+        const uint32_t hi01 = __builtin_amdgcn_perm(v[4 * u + 1], v[4 * u], 0x07060302u);
+        const uint32_t lo23 = __builtin_amdgcn_perm(v[4 * u + 3], v[4 * u + 2], 0x05040100u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(v[4 * u + 3], v[4 * u + 2], 0x07060302u);
+        w_lo[u] = cvt4(lo01, lo23, s_lo);
+        w_hi[u] = cvt4(hi01, hi23, s_hi);
+    }
+    if (__any(b_lo >= 254u || b_hi >= 254u)) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            w_lo[u] = b_lo == 255u ? 0x7F7F7F7Fu : nan_bytes_to_max(w_lo[u]);
+            w_hi[u] = b_hi == 255u ? 0x7F7F7F7Fu : nan_bytes_to_max(w_hi[u]);
+        }
+    }
+    uint8_t* qc = q_col + (n0 + 2 * cp) * M + m0 + 32 * br;
+    *reinterpret_cast<uint4*>(qc) = make_uint4(w_lo[0], w_lo[1], w_lo[2], w_lo[3]);
+    *reinterpret_cast<uint4*>(qc + 16) = make_uint4(w_lo[4], w_lo[5], w_lo[6], w_lo[7]);
+    *reinterpret_cast<uint4*>(qc + M) = make_uint4(w_hi[0], w_hi[1], w_hi[2], w_hi[3]);
+    *reinterpret_cast<uint4*>(qc + M + 16) = make_uint4(w_hi[4], w_hi[5], w_hi[6], w_hi[7]);
+
+    const int64_t sbr = m0 / 32 + br;
+    uint16_t sv = uint16_t(b_lo | (b_hi << 8));
+    if (kGrouped && sbr >= tail_br) sv = 0;
+    *reinterpret_cast<uint16_t*>(s_col + sbr * N + n0 + 2 * cp) = sv;
+}
+
+__global__ __launch_bounds__(kThreads)
+void offs_validate_kernel(const int32_t* __restrict__ offs, int32_t G, int64_t M, int32_t* __restrict__ err) {
+    validate_offsets(offs, G, M, err);
+}
+
+}  // namespace
+
+hipError_t launch_dual_axis(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x,
+                            uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                            const int32_t* offs, int32_t G, int32_t* err, bool grouped,
+                            hipStream_t stream) {
+    const uint32_t tiles_n = uint32_t(N / kTile);
+    const uint32_t tiles = uint32_t((M / kTile) * (N / kTile));
+    if (grouped)
+        hipLaunchKernelGGL(dual_axis_kernel<true>, dim3(tiles), dim3(kThreads), 0, stream,
+                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles, offs, G, err);
+    else
+        hipLaunchKernelGGL(dual_axis_kernel<false>, dim3(tiles), dim3(kThreads), 0, stream,
+                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles,
+                           static_cast<const int32_t*>(nullptr), 0, static_cast<int32_t*>(nullptr));
+    return hipGetLastError();
+}
+
+hipError_t launch_offs_validate(const int32_t* offs, int32_t G, int64_t M, int32_t* err,
+                                hipStream_t stream) {
+    hipLaunchKernelGGL(offs_validate_kernel, dim3(1), dim3(kThreads), 0, stream, offs, G, M, err);
+    return hipGetLastError();
+}
+
+}  // namespace mxq

@@ -1,0 +1,168 @@
+// mxq_abi.cpp -- the C ABI declared in include/mxq.h.
+//
+// Every entry point validates its arguments on the host, in the order the
+// header documents, before enqueuing anything; a nonzero status therefore
+// means no output byte was written.  Nothing here allocates, synchronizes or
+// keeps state.
+#include "../../include/mxq.h"
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mxq_kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr uint64_t kMaxThreads = 0xFFFFFFFFull - 256;   // grid.x * block.x must fit 32 bits
+
+struct Span {
+    uintptr_t p;
+    uint64_t n;   // bytes
+};
+
+bool overlap(const Span& a, const Span& b) {
+    return a.n != 0 && b.n != 0 && a.p < b.p + b.n && b.p < a.p + a.n;
+}
+
+bool any_overlap(const Span* s, int k) {
+    for (int i = 0; i < k; ++i)
+        for (int j = i + 1; j < k; ++j)
+            if (overlap(s[i], s[j])) return true;
+    return false;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+uintptr_t addr(const void* p) { return reinterpret_cast<uintptr_t>(p); }
+
+// Bytes spanned by a [rows, cols] matrix with row pitch ld (elements).
+uint64_t matrix_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t esz) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return uint64_t((rows - 1) * ld + cols) * uint64_t(esz);
+}
+
+int check_dual(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x, int32_t block_size,
+               int32_t scaling_mode, const uint8_t* q_row, const uint8_t* s_row,
+               const uint8_t* q_col, const uint8_t* s_col) {
+    const bool empty = M == 0 || N == 0;   // empty buffers may be NULL
+    if (!empty && (!x || !q_row || !s_row || !q_col || !s_col)) return MX_E_NULL;
+    if (block_size != 32) return MX_E_BLOCK;
+    if (scaling_mode != MX_SCALE_RCEIL) return MX_E_MODE;
+    if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim || M % 128 != 0 || N % 128 != 0)
+        return MX_E_SHAPE;
+    if (uint64_t(M / 128) * uint64_t(N / 128) * 256 > kMaxThreads) return MX_E_SHAPE;
+    if (ld_x < N || ld_x % 8 != 0 || ld_x > (int64_t(1) << 40)) return MX_E_STRIDE;
+    if (!empty && (!aligned(x, 16) || !aligned(q_row, 16) || !aligned(s_row, 16) ||
+                   !aligned(q_col, 16) || !aligned(s_col, 16)))
+        return MX_E_ALIGN;
+    return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mx_status_string(int status) {
+    switch (status) {
+        case MX_OK: return "MX_OK: success";
+        case MX_E_NULL: return "MX_E_NULL: a required pointer is NULL";
+        case MX_E_DTYPE: return "MX_E_DTYPE: unsupported element type (fp32 or bf16 only)";
+        case MX_E_BLOCK: return "MX_E_BLOCK: unsupported block size (32 for MXFP8, 16 for MX9)";
+        case MX_E_MODE: return "MX_E_MODE: unsupported scaling mode (RCEIL only)";
+        case MX_E_SHAPE: return "MX_E_SHAPE: unsupported shape (MXFP8 needs M, N multiples of 128)";
+        case MX_E_STRIDE: return "MX_E_STRIDE: row pitch smaller than the row or misaligned";
+        case MX_E_ALIGN: return "MX_E_ALIGN: pointer misaligned";
+        case MX_E_OVERLAP: return "MX_E_OVERLAP: buffers of one call overlap";
+        case MX_E_LAUNCH: return "MX_E_LAUNCH: kernel launch failed";
+        default: return "unknown mx_status";
+    }
+}
+
+int mx_quantize_2d_dual(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x,
+                        int32_t block_size, int32_t scaling_mode,
+                        uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                        void* stream) {
+    int rc = check_dual(x, M, N, ld_x, block_size, scaling_mode, q_row, s_row, q_col, s_col);
+    if (rc != MX_OK) return rc;
+    const uint64_t mn = uint64_t(M) * uint64_t(N);
+    const Span s[5] = {{addr(x), matrix_bytes(M, N, ld_x, 2)}, {addr(q_row), mn}, {addr(s_row), mn / 32},
+                       {addr(q_col), mn}, {addr(s_col), mn / 32}};
+    if (any_overlap(s, 5)) return MX_E_OVERLAP;
+    if (M == 0 || N == 0) return MX_OK;
+    hipError_t e = mxq::launch_dual_axis(x, M, N, ld_x, q_row, s_row, q_col, s_col, nullptr, 0,
+                                         nullptr, false, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+}
+
+int mx_quantize_grouped(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x,
+                        int32_t block_size, int32_t scaling_mode,
+                        const int32_t* offs, int32_t G,
+                        uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                        int32_t* err, void* stream) {
+    int rc = check_dual(x, M, N, ld_x, block_size, scaling_mode, q_row, s_row, q_col, s_col);
+    if (rc != MX_OK) return rc;
+    if (G < 0) return MX_E_SHAPE;
+    if (G > 0 && !offs) return MX_E_NULL;
+    if (G > 0 && !aligned(offs, 4)) return MX_E_ALIGN;
+    if (err && !aligned(err, 4)) return MX_E_ALIGN;
+    const uint64_t mn = uint64_t(M) * uint64_t(N);
+    const Span s[7] = {{addr(x), matrix_bytes(M, N, ld_x, 2)}, {addr(q_row), mn}, {addr(s_row), mn / 32},
+                       {addr(q_col), mn}, {addr(s_col), mn / 32},
+                       {addr(offs), G > 0 ? uint64_t(G) * 4 : 0}, {addr(err), err ? 4u : 0u}};
+    if (any_overlap(s, 7)) return MX_E_OVERLAP;
+    hipError_t e = hipSuccess;
+    if (M == 0 || N == 0) {
+        if (err) e = mxq::launch_offs_validate(offs, G, M, err, static_cast<hipStream_t>(stream));
+    } else {
+        e = mxq::launch_dual_axis(x, M, N, ld_x, q_row, s_row, q_col, s_col, offs, G, err, true,
+                                  static_cast<hipStream_t>(stream));
+    }
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+}
+
+int mx9_pack(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld_x,
+             int32_t block_size, int8_t* q, uint8_t* max_exp, uint8_t* prime, void* stream) {
+    const bool empty = rows == 0 || cols == 0;   // empty buffers may be NULL
+    if (!empty && (!x || !q || !max_exp || !prime)) return MX_E_NULL;
+    if (dtype != MX_DTYPE_F32 && dtype != MX_DTYPE_BF16) return MX_E_DTYPE;
+    if (block_size != 16) return MX_E_BLOCK;
+    if (rows < 0 || cols < 0 || rows > (int64_t(1) << 40) || cols > kMaxDim) return MX_E_SHAPE;
+    const uint64_t nb = uint64_t(rows) * uint64_t((cols + 15) / 16);
+    if (nb > kMaxThreads) return MX_E_SHAPE;
+    if (ld_x < cols || ld_x > (int64_t(1) << 40)) return MX_E_STRIDE;
+    const int64_t esz = dtype == MX_DTYPE_F32 ? 4 : 2;
+    if (!empty && (!aligned(x, uintptr_t(esz)) || !aligned(q, 16))) return MX_E_ALIGN;
+    const Span s[4] = {{addr(x), matrix_bytes(rows, cols, ld_x, esz)}, {addr(q), nb * 16},
+                       {addr(max_exp), nb}, {addr(prime), nb}};
+    if (any_overlap(s, 4)) return MX_E_OVERLAP;
+    if (nb == 0) return MX_OK;
+    hipError_t e = mxq::launch_mx9_pack(x, dtype, rows, cols, ld_x, q, max_exp, prime,
+                                        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+}
+
+int mx9_unpack(const int8_t* q, const uint8_t* max_exp, const uint8_t* prime,
+               int64_t rows, int64_t cols, int32_t block_size, int32_t out_dtype,
+               void* y, int64_t ld_y, void* stream) {
+    const bool empty = rows == 0 || cols == 0;   // empty buffers may be NULL
+    if (!empty && (!q || !max_exp || !prime || !y)) return MX_E_NULL;
+    if (out_dtype != MX_DTYPE_F32 && out_dtype != MX_DTYPE_BF16) return MX_E_DTYPE;
+    if (block_size != 16) return MX_E_BLOCK;
+    if (rows < 0 || cols < 0 || rows > (int64_t(1) << 40) || cols > kMaxDim) return MX_E_SHAPE;
+    const uint64_t nb = uint64_t(rows) * uint64_t((cols + 15) / 16);
+    if (nb > kMaxThreads) return MX_E_SHAPE;
+    if (ld_y < cols || ld_y > (int64_t(1) << 40)) return MX_E_STRIDE;
+    const int64_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
+    if (!empty && (!aligned(q, 16) || !aligned(y, uintptr_t(esz)))) return MX_E_ALIGN;
+    const Span s[4] = {{addr(q), nb * 16}, {addr(max_exp), nb}, {addr(prime), nb},
+                       {addr(y), matrix_bytes(rows, cols, ld_y, esz)}};
+    if (any_overlap(s, 4)) return MX_E_OVERLAP;
+    if (nb == 0) return MX_OK;
+    hipError_t e = mxq::launch_mx9_unpack(q, max_exp, prime, rows, cols, out_dtype, y, ld_y,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+}
+
+}  // extern "C"

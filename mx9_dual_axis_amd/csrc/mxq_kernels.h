@@ -1,0 +1,33 @@
+// Internal launch interface between the C-ABI layer (mxq_abi.cpp) and the
+// HIP kernels.  Arguments arrive already validated; each launcher enqueues
+// on the given stream and returns the launch's hipError_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+// Fused dual-axis MXFP8 cast of a bf16 [M, N] matrix (M, N > 0, multiples
+// of 128).  offs == nullptr selects the dense cast; otherwise G >= 0 group
+// ends drive the uncovered-tail rule and *err (when non-null) receives the
+// offset validation code.
+hipError_t launch_dual_axis(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x,
+                            uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                            const int32_t* offs, int32_t G, int32_t* err, bool grouped,
+                            hipStream_t stream);
+
+// Offset validation alone, for a grouped call on an empty matrix.
+hipError_t launch_offs_validate(const int32_t* offs, int32_t G, int64_t M, int32_t* err,
+                                hipStream_t stream);
+
+// MX9 pack of [rows, cols] (rows, cols > 0); dtype 0 = fp32, 1 = bf16.
+hipError_t launch_mx9_pack(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                           int8_t* q, uint8_t* max_exp, uint8_t* prime, hipStream_t stream);
+
+// MX9 unpack to [rows, cols] (rows, cols > 0); out_dtype 0 = fp32, 1 = bf16.
+hipError_t launch_mx9_unpack(const int8_t* q, const uint8_t* max_exp, const uint8_t* prime,
+                             int64_t rows, int64_t cols, int out_dtype, void* y, int64_t ld_y,
+                             hipStream_t stream);
+
+}  // namespace mxq

@@ -1,0 +1,115 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every function
+include/mxq.h declares, and its host-side validation answers before any
+launch (so nothing here needs a GPU: invalid calls never reach the device,
+and empty calls launch nothing)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mx9_dual_axis_amd as mxq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+FAKE = 1 << 20          # never dereferenced: every call below fails validation or is empty
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|char|void)\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(["mx_quantize_2d_dual", "mx_quantize_grouped", "mx9_pack", "mx9_unpack",
+                                  "mx_status_string"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mxq.library()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", mxq.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\s[TW]\s(\w+)$", out, flags=re.M))
+    for name in _declared():
+        assert name in exported, name
+
+
+def test_status_strings():
+    for code in range(10):
+        s = mxq.status_string(code)
+        assert s.startswith("MX_"), s
+    assert "unknown" in mxq.status_string(99)
+
+
+def _dual(**kw):
+    a = dict(x=FAKE, M=256, N=256, ld=256, bs=32, mode=0, qr=FAKE * 2, sr=FAKE * 3, qc=FAKE * 4, sc=FAKE * 5)
+    a.update(kw)
+    return mxq.library().mx_quantize_2d_dual(a["x"], a["M"], a["N"], a["ld"], a["bs"], a["mode"],
+                                             a["qr"], a["sr"], a["qc"], a["sc"], None)
+
+
+def test_dual_validation_codes():
+    assert _dual(x=None) == 1
+    assert _dual(bs=16) == 3
+    assert _dual(mode=1) == 4
+    assert _dual(M=200) == 5 and _dual(N=100) == 5 and _dual(M=-128) == 5
+    assert _dual(M=1 << 31) == 5
+    assert _dual(ld=128) == 6 and _dual(ld=260) == 6
+    assert _dual(qc=FAKE * 4 + 8) == 7
+    assert _dual(qc=FAKE * 2 + 4096) == 8            # q_col starts inside q_row
+    assert _dual(sr=FAKE + 1024) == 8                # s_row inside the input
+    assert _dual(M=0, x=None, qr=None, sr=None, qc=None, sc=None) == 0     # empty: no-op, no launch
+
+
+def test_grouped_validation_codes():
+    lib = mxq.library()
+
+    def g(offs=FAKE * 6, G=4, err=FAKE * 7, **kw):
+        a = dict(x=FAKE, M=256, N=256, ld=256, qr=FAKE * 2, sr=FAKE * 3, qc=FAKE * 4, sc=FAKE * 5)
+        a.update(kw)
+        return lib.mx_quantize_grouped(a["x"], a["M"], a["N"], a["ld"], 32, 0, offs, G,
+                                       a["qr"], a["sr"], a["qc"], a["sc"], err, None)
+    assert g(G=-1) == 5
+    assert g(offs=None) == 1
+    assert g(offs=FAKE * 6 + 2) == 7
+    assert g(err=FAKE * 7 + 1) == 7
+    assert g(offs=FAKE * 2 + 8) == 8                 # offsets inside q_row
+    assert g(err=FAKE * 5 + 4) == 8                  # err inside s_col
+    assert g(M=0, G=0, err=None, x=None, qr=None, sr=None, qc=None, sc=None) == 0
+
+
+def test_mx9_validation_codes():
+    lib = mxq.library()
+
+    def pack(dtype=0, rows=4, cols=64, ld=64, bs=16, x=FAKE, q=FAKE * 2, e=FAKE * 3, p=FAKE * 4):
+        return lib.mx9_pack(x, dtype, rows, cols, ld, bs, q, e, p, None)
+
+    def unpack(rows=4, cols=64, bs=16, od=0, y=FAKE * 5, ld=64, q=FAKE * 2, e=FAKE * 3, p=FAKE * 4):
+        return lib.mx9_unpack(q, e, p, rows, cols, bs, od, y, ld, None)
+    assert pack(x=None) == 1 and pack(dtype=2) == 2 and pack(bs=32) == 3 and pack(rows=-1) == 5
+    assert pack(ld=32) == 6 and pack(x=FAKE + 2) == 7 and pack(q=FAKE * 2 + 4) == 7
+    assert pack(e=FAKE + 16) == 8
+    assert pack(rows=0, x=None, q=None, e=None, p=None) == 0
+    assert unpack(y=None) == 1 and unpack(od=3) == 2 and unpack(bs=8) == 3 and unpack(cols=-5) == 5
+    assert unpack(ld=10) == 6 and unpack(y=FAKE * 5 + 2) == 7 and unpack(q=FAKE * 2 + 8) == 7
+    assert unpack(y=FAKE * 2 + 64) == 8
+    assert unpack(cols=0, y=None, q=None, e=None, p=None) == 0
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    monkeypatch.setattr(mxq, "LIB_PATH", "/nonexistent/libmxq.so")
+    monkeypatch.setattr(mxq, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        mxq.library()
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "mx9_dual_axis_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b|liboracle|mx_oracle|oref_", src, flags=re.M), f

@@ -1,0 +1,223 @@
+"""GPU parity of MX9 pack / unpack (mx9_pack, mx9_unpack) against the CPU
+oracle: q, max_exp, prime and the unpacked values must be equal bit for bit.
+Format: AMD-AGI/ALTO PR #33 "feat: mx9: add fused MX9 quantization kernel
+with pack/unpack"."""
+import numpy as np
+import pytest
+import torch
+
+import mx9_dual_axis_amd as mxq
+import oracle
+from helpers import bf16_to_dev, host, require_gpu, sample_rows, say
+from mx9_dual_axis_amd import synth
+
+pytestmark = pytest.mark.gpu
+THREADS = 16
+
+
+def _to_dev(x):
+    if x.dtype == np.uint16:
+        return bf16_to_dev(x)
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda:0")
+
+
+def _check_pack(x, tag, dev_x=None):
+    rows, cols = x.shape
+    xd = _to_dev(x) if dev_x is None else dev_x
+    nb = rows * ((cols + 15) // 16)
+    out = (torch.full((nb, 16), 0x5A, dtype=torch.int8, device=xd.device),
+           torch.full((nb,), 0xA5, dtype=torch.uint8, device=xd.device),
+           torch.full((nb, 1), 0xA5, dtype=torch.uint8, device=xd.device))
+    q, e, p = mxq.mx9_pack(xd, out=out)
+    torch.cuda.synchronize()
+    wq, we, wp = oracle.mx9_pack(x, threads=THREADS)
+    for name, g, w in (("q", q, wq), ("max_exp", e, we), ("prime", p, wp)):
+        g = host(g)
+        bad = np.count_nonzero(g != w)
+        if bad:
+            i = np.argwhere(g != w)[0]
+            pytest.fail(f"{tag}: {name} differs in {bad} entries; first {i.tolist()} got {g[tuple(i)]} want {w[tuple(i)]}")
+    return q, e, p, (wq, we, wp)
+
+
+def _check_unpack(q, e, p, rows, cols, tag, out_dtype="fp32"):
+    td = torch.float32 if out_dtype == "fp32" else torch.bfloat16
+    y = mxq.mx9_unpack(q, e, p, rows, cols, out_dtype=td)
+    torch.cuda.synchronize()
+    want = oracle.mx9_unpack(host(q), host(e), host(p), rows, cols, out_dtype, threads=THREADS)
+    g = host(y)
+    gb = g.view(np.uint32) if out_dtype == "fp32" else g
+    wb = want.view(np.uint32) if out_dtype == "fp32" else want
+    bad = np.count_nonzero(gb != wb)
+    if bad:
+        i = np.argwhere(gb != wb)[0]
+        pytest.fail(f"{tag}: unpack {out_dtype} differs in {bad}; first {i.tolist()} got {hex(gb[tuple(i)])} want {hex(wb[tuple(i)])}")
+    return y
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("rows,cols", [(16, 64), (64, 1024), (33, 200), (7, 5), (128, 4096), (1, 16)])
+def test_pack_unpack_parity(dtype, rows, cols):
+    require_gpu()
+    say(f"mx9 parity {dtype} [{rows}, {cols}]")
+    x = synth.mx9_weights(rows, cols, rows * 31 + cols, dtype)
+    q, e, p, _ = _check_pack(x, f"{dtype} {rows}x{cols}")
+    for od in ("fp32", "bf16"):
+        _check_unpack(q, e, p, rows, cols, f"{dtype} {rows}x{cols}", od)
+
+
+def test_special_values_and_subnormals():
+    require_gpu()
+    say("mx9 special values")
+    g = np.random.default_rng(3)
+    x = synth.mx9_weights(64, 256, 3)
+    bits = x.view(np.uint32)
+    bits[0, :16] = 0                                          # zeros
+    bits[1, :16] = g.integers(0, 1 << 23, 16)                 # subnormal block
+    bits[1, 16:32] = g.integers(0, 1 << 23, 16) | (1 << 31)
+    bits[2, 3] = 0x7F800000; bits[2, 20] = 0xFF800000         # +-Inf
+    bits[3, 7] = 0x7FC00000; bits[3, 40] = 0xFFC12345         # NaNs
+    bits[4, :16] = 0x7F7FFFFF                                 # fp32 max
+    bits[5, :16] = [0x3FFF0000, 0x3F810000, 0x3F830000, 0x3F7F8000] * 4   # clamp and ties
+    bits[6, :] = (g.integers(1, 255, 256) << 23) | g.integers(0, 1 << 23, 256)  # all binades
+    q, e, p, _ = _check_pack(x, "specials fp32")
+    _check_unpack(q, e, p, 64, 256, "specials", "fp32")
+    _check_unpack(q, e, p, 64, 256, "specials", "bf16")
+    xb = synth.special_matrix(64, 256, 4)
+    q, e, p, _ = _check_pack(xb, "specials bf16")
+    _check_unpack(q, e, p, 64, 256, "specials bf16", "bf16")
+
+
+def test_every_bf16_pattern_lone():
+    require_gpu()
+    say("mx9 lone bf16 patterns")
+    pats = np.arange(65536, dtype=np.uint32)
+    x = np.zeros((65536, 16), np.uint16)
+    x[pats, pats % 16] = pats.astype(np.uint16)
+    q, e, p, _ = _check_pack(x, "lone patterns")
+    _check_unpack(q, e, p, 65536, 16, "lone patterns", "bf16")
+    _check_unpack(q, e, p, 65536, 16, "lone patterns", "fp32")
+
+
+def test_exhaustive_unpack():
+    require_gpu()
+    say("mx9 exhaustive unpack")
+    S = np.repeat(np.arange(256), 2 * 256)
+    P = np.tile(np.repeat(np.arange(2), 256), 256)
+    Q = np.tile(np.arange(-128, 128), 512)
+    nb = S.size // 16
+    q = torch.from_numpy(Q.astype(np.int8).reshape(nb, 16)).cuda()
+    e = torch.from_numpy(S.reshape(nb, 16)[:, 0].astype(np.uint8)).cuda()
+    p = torch.from_numpy((P.reshape(nb, 16)[:, 0] * 0xFF).astype(np.uint8).reshape(nb, 1)).cuda()
+    for od in ("fp32", "bf16"):
+        _check_unpack(q, e, p, 1, S.size, "exhaustive", od)
+        _check_unpack(q, e, p, nb, 16, "exhaustive rows", od)
+
+
+def test_strided_and_unaligned_inputs():
+    require_gpu()
+    say("mx9 strided input and output")
+    wide = synth.mx9_weights(48, 300, 5)
+    xd = _to_dev(wide)[:, 7:263]                              # ld 300, start unaligned
+    q, e, p, _ = _check_pack(np.ascontiguousarray(wide[:, 7:263]), "strided fp32", dev_x=xd)
+    wideb = synth.mx9_weights(48, 300, 6, "bf16")
+    xdb = _to_dev(wideb)[:, 16:272]                           # ld 300 (600 B rows): not 16-byte rows
+    _check_pack(np.ascontiguousarray(wideb[:, 16:272]), "strided bf16", dev_x=xdb)
+    # unpack into a wider output: only cols columns are written
+    yw = torch.full((48, 300), 7.0, dtype=torch.float32, device="cuda:0")
+    mxq.mx9_unpack(q, e, p, 48, 256, out=yw)
+    torch.cuda.synchronize()
+    want = oracle.mx9_unpack(host(q), host(e), host(p), 48, 256, "fp32")
+    got = host(yw)
+    assert np.array_equal(got[:, :256].view(np.uint32), want.view(np.uint32))
+    assert (got[:, 256:] == 7.0).all()
+
+
+def test_rejections_and_empty():
+    dev = require_gpu()
+    say("mx9 rejections")
+    with pytest.raises(mxq.MXError) as ei:
+        mxq.mx9_pack(torch.zeros((4, 16), dtype=torch.float16, device=dev))
+    assert ei.value.status == 2
+    with pytest.raises(mxq.MXError) as ei:
+        mxq.mx9_pack(torch.zeros((4, 16), dtype=torch.float32, device=dev), block_size=32)
+    assert ei.value.status == 3
+    q, e, p = mxq.mx9_pack(torch.zeros((4, 16), dtype=torch.float32, device=dev))
+    with pytest.raises(mxq.MXError) as ei:
+        mxq.mx9_unpack(q, e, p, 4, 16, out_dtype=torch.float16)
+    assert ei.value.status == 2
+    q, e, p = mxq.mx9_pack(torch.zeros((0, 16), dtype=torch.float32, device=dev))
+    assert q.shape == (0, 16)
+    y = mxq.mx9_unpack(q, e, p, 0, 16)
+    assert y.shape == (0, 16)
+
+
+def test_graph_capture():
+    require_gpu()
+    say("mx9 in a captured graph")
+    x = synth.mx9_weights(64, 512, 8, "bf16")
+    xd = _to_dev(x)
+    q, e, p = mxq.mx9_pack(xd)
+    y = mxq.mx9_unpack(q, e, p, 64, 512, out_dtype=torch.bfloat16)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mxq.mx9_pack(xd, out=(q, e, p))
+        mxq.mx9_unpack(q, e, p, 64, 512, out=y)
+    wq, we, wp = oracle.mx9_pack(x)
+    wy = oracle.mx9_unpack(wq, we, wp, 64, 512, "bf16")
+    for rep in range(3):
+        q.fill_(3); e.fill_(3); p.fill_(3); y.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(q), wq) and np.array_equal(host(e), we) and np.array_equal(host(p), wp)
+        assert np.array_equal(host(y), wy), rep
+
+
+# ---------------------------------------------------------------- full sizes
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_full_size_weights_sampled(dtype):
+    require_gpu()
+    say(f"mx9 full size weights [4096, 14336] {dtype}: sampled parity, SNR")
+    x = synth.mx9_weights(4096, 14336, 4, dtype)
+    xd = _to_dev(x)
+    q, e, p = mxq.mx9_pack(xd)
+    y = mxq.mx9_unpack(q, e, p, 4096, 14336, out_dtype=torch.float32 if dtype == "fp32" else torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = sample_rows(4096, 64, 4)
+    nbr = 14336 // 16
+    sel = (rows[:, None] * nbr + np.arange(nbr)[None, :]).reshape(-1)
+    wq, we, wp = oracle.mx9_pack(np.ascontiguousarray(x[rows]), threads=THREADS)
+    hq, he, hp = host(q), host(e), host(p)
+    assert np.array_equal(hq[sel], wq) and np.array_equal(he[sel], we) and np.array_equal(hp[sel], wp)
+    wy = oracle.mx9_unpack(wq, we, wp, len(rows), 14336, dtype, threads=THREADS)
+    hy = host(y)[rows]
+    assert np.array_equal(hy.view(np.uint32 if dtype == "fp32" else np.uint16),
+                          wy.view(np.uint32 if dtype == "fp32" else np.uint16))
+    # whole-matrix properties: range of the exponent byte and round-trip quality
+    assert int(e.min()) >= 1 and int(e.max()) <= 254 and int(q.abs().max()) <= 127
+    xf = xd.float()
+    snr = 10 * torch.log10((xf * xf).sum() / ((xf - y.float()) ** 2).sum()).item()
+    say(f"  SNR {dtype}: {snr:.2f} dB")
+    assert snr > 40.0
+
+
+def test_full_size_stress_sampled():
+    require_gpu()
+    say("mx9 full size stress bf16 [32768, 8192]: sampled parity")
+    x = synth.stress()
+    xd = _to_dev(x)
+    q, e, p = mxq.mx9_pack(xd)
+    y = mxq.mx9_unpack(q, e, p, 32768, 8192, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    special = np.unique(np.argwhere((x & 0x7F80) == 0x7F80)[:, 0])
+    rows = np.unique(np.concatenate([sample_rows(32768, 48, 5), special[:64]]))
+    nbr = 8192 // 16
+    sel = (rows[:, None] * nbr + np.arange(nbr)[None, :]).reshape(-1)
+    wq, we, wp = oracle.mx9_pack(np.ascontiguousarray(x[rows]), threads=THREADS)
+    hq, he, hp = host(q), host(e), host(p)
+    assert np.array_equal(hq[sel], wq) and np.array_equal(he[sel], we) and np.array_equal(hp[sel], wp)
+    wy = oracle.mx9_unpack(wq, we, wp, len(rows), 8192, "bf16", threads=THREADS)
+    assert np.array_equal(host(y)[rows], wy)
+    assert int((e == 255).sum()) >= 1

@@ -12,21 +12,28 @@
 //              packed u16 max of the sign-masked bf16 patterns followed by a
 //              two-step DPP quad reduction.  Masking the sign makes the
 //              integer order NaN > Inf > finite, so the special cases need no
-//              per-element test.
-//   * LDS    : the tile is written once (32 KiB) for the colwise pass.
-//   * colwise: each thread owns a column pair and one 32-row block: 32 LDS
-//              dwords, a packed u16 max gives both column maxima at once;
+//              per-element test.  The cast runs from registers.
+//   * LDS    : the tile is written once (32 KiB).  The column-pair index of
+//              each dword is XORed with the row's 16-row chunk (bits 3..5), so
+//              the colwise reads below are bank-conflict free.
+//   * colwise: a unit is (column pair, 16-row chunk); each thread takes two.
+//              A packed u16 max over 16 LDS dwords plus one DPP step between
+//              the two chunks of a 32-row block gives both column maxima;
 //              v_perm regroups (row m, row m+1) pairs of one column so the
-//              packed scaled cast yields m-contiguous bytes, stored as two
-//              16-byte writes per column of the transposed output.
+//              packed scaled cast yields m-contiguous bytes.  The eight lanes
+//              that share a column pair hold its eight chunks, so every
+//              16-byte store of a wave lands in full 128-byte lines of the
+//              transposed output.
 //   * cast   : v_cvt_scalef32_pk_fp8_bf16 divides by the E8M0 scale 2^(b-127)
 //              given as fp32 bits b<<23 (byte 0 acts as 2^-127, i.e. the 2^127
 //              multiplier) and rounds to nearest even; it does not saturate,
 //              so the colwise Inf block (scale 254) maps its NaN bytes to
 //              +-448 afterwards, and poisoned blocks are overwritten with 0x7F.
-//   * order  : workgroups are dispatched round-robin over the 8 XCDs; each XCD
-//              is given a contiguous range of tiles so that the tiles sharing
-//              an s_row cache line are written through the same L2.
+//   * order  : tiles are visited in a diagonal order (consecutive workgroups
+//              take consecutive tile rows, each shifted one tile column), which
+//              spreads the concurrently active row segments of the input and
+//              of both outputs over the HBM channels better than row-major or
+//              column-major order (measured).
 #include "mxq_kernels.h"
 
 #include <limits.h>
@@ -36,7 +43,6 @@ namespace {
 
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
-constexpr uint32_t kXcds = 8;
 
 typedef short v2i16 __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
@@ -120,11 +126,11 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
 
     const uint32_t t = threadIdx.x;
     const uint32_t bid = blockIdx.x;
-    const uint32_t per = tiles / kXcds, rem = tiles % kXcds;
-    const uint32_t xcd = bid % kXcds, loc = bid / kXcds;
-    const uint32_t tile = xcd * per + min(xcd, rem) + loc;
-    const int64_t m0 = int64_t(tile / tiles_n) * kTile;
-    const int64_t n0 = int64_t(tile % tiles_n) * kTile;
+    const uint32_t tiles_m = tiles / tiles_n;
+    const uint32_t tm = bid % tiles_m;
+    const uint32_t tn = (bid / tiles_m + tm) % tiles_n;
+    const int64_t m0 = int64_t(tm) * kTile;
+    const int64_t n0 = int64_t(tn) * kTile;
 
     // first block row of the uncovered tail (grouped only)
     int64_t tail_br = M / 32;
@@ -150,7 +156,7 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const uint32_t r = 16u * k + rsub;
-        lds_tile[r * 16u + (t & 15u)] = d[k];
+        lds_tile[r * 16u + ((t & 15u) ^ (((r >> 4) & 7u) << 1))] = d[k];
         const uint32_t mx = pk_max_u16(pk_max_u16(d[k].x & 0x7FFF7FFFu, d[k].y & 0x7FFF7FFFu),
                                        pk_max_u16(d[k].z & 0x7FFF7FFFu, d[k].w & 0x7FFF7FFFu));
         uint32_t a = max(mx & 0xFFFFu, mx >> 16);
@@ -170,47 +176,55 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
     if (t < kTile)
         *reinterpret_cast<uint32_t*>(s_row + (m0 + t) * (N / 32) + n0 / 32) = lds_srow[t];
 
-    // ---- colwise 32x1 pass: columns 2cp, 2cp+1 of rows 32br .. 32br+31 ----
-    const uint32_t cp = t & 63u;
-    const uint32_t br = t >> 6;
+    // ---- colwise 32x1 pass ----
+    // Unit = (column pair cp, 16-row chunk c); each thread takes two units.
+    // Eight lanes share a column pair and hold its eight chunks, so each
+    // 16-byte store of a column lands in one full 128-byte line per 8 lanes.
+    // The two chunks of a 32-row block sit in lanes l, l^1 (one DPP step).
+    const uint32_t lane = t & 63u, wave = t >> 6;
+    const uint32_t c = lane & 7u;
     const uint32_t* lt = reinterpret_cast<const uint32_t*>(lds_tile);
-    uint32_t v[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = lt[(32u * br + i) * 64u + cp];
-    uint32_t cm = 0;
+    for (int u = 0; u < 2; ++u) {
+        const uint32_t cp = ((lane >> 3) & 7u) + 8u * (wave + 4u * u);
+        const uint32_t* src = lt + (16u * c) * 64u + (cp ^ (c << 3));
+        uint32_t v[16];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) cm = pk_max_u16(cm, v[i] & 0x7FFF7FFFu);
-    const uint32_t b_lo = col_scale(cm & 0xFFFFu);
-    const uint32_t b_hi = col_scale(cm >> 16);
-    const float s_lo = e8m0_operand(b_lo), s_hi = e8m0_operand(b_hi);
-    uint32_t w_lo[8], w_hi[8];
+        for (int i = 0; i < 16; ++i) v[i] = src[i * 64];
+        uint32_t cm = 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        // (row 4u, row 4u+1) and (row 4u+2, row 4u+3) of each column
-        const uint32_t lo01 = __builtin_amdgcn_perm(v[4 * u + 1], v[4 * u], 0x05040100u);
-        const uint32_t hi01 = __builtin_amdgcn_perm(v[4 * u + 1], v[4 * u], 0x07060302u);
-        const uint32_t lo23 = __builtin_amdgcn_perm(v[4 * u + 3], v[4 * u + 2], 0x05040100u);
-        const uint32_t hi23 = __builtin_amdgcn_perm(v[4 * u + 3], v[4 * u + 2], 0x07060302u);
-        w_lo[u] = cvt4(lo01, lo23, s_lo);
-        w_hi[u] = cvt4(hi01, hi23, s_hi);
-    }
-    if (__any(b_lo >= 254u || b_hi >= 254u)) {
+        for (int i = 0; i < 16; ++i) cm = pk_max_u16(cm, v[i] & 0x7FFF7FFFu);
+        cm = pk_max_u16(cm, uint32_t(__builtin_amdgcn_mov_dpp(int(cm), 0xB1, 0xF, 0xF, true)));  // lane ^ 1
+        const uint32_t b_lo = col_scale(cm & 0xFFFFu);
+        const uint32_t b_hi = col_scale(cm >> 16);
+        const float s_lo = e8m0_operand(b_lo), s_hi = e8m0_operand(b_hi);
+        uint32_t w_lo[4], w_hi[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            w_lo[u] = b_lo == 255u ? 0x7F7F7F7Fu : nan_bytes_to_max(w_lo[u]);
-            w_hi[u] = b_hi == 255u ? 0x7F7F7F7Fu : nan_bytes_to_max(w_hi[u]);
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t lo01 = __builtin_amdgcn_perm(v[4 * q + 1], v[4 * q], 0x05040100u);
+            const uint32_t hi01 = __builtin_amdgcn_perm(v[4 * q + 1], v[4 * q], 0x07060302u);
+            const uint32_t lo23 = __builtin_amdgcn_perm(v[4 * q + 3], v[4 * q + 2], 0x05040100u);
+            const uint32_t hi23 = __builtin_amdgcn_perm(v[4 * q + 3], v[4 * q + 2], 0x07060302u);
+            w_lo[q] = cvt4(lo01, lo23, s_lo);
+            w_hi[q] = cvt4(hi01, hi23, s_hi);
+        }
+        if (__any(b_lo >= 254u || b_hi >= 254u)) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                w_lo[q] = b_lo == 255u ? 0x7F7F7F7Fu : nan_bytes_to_max(w_lo[q]);
+                w_hi[q] = b_hi == 255u ? 0x7F7F7F7Fu : nan_bytes_to_max(w_hi[q]);
+            }
+        }
+        uint8_t* qc = q_col + (n0 + 2 * cp) * M + m0 + 16 * c;
+        *reinterpret_cast<uint4*>(qc) = make_uint4(w_lo[0], w_lo[1], w_lo[2], w_lo[3]);
+        *reinterpret_cast<uint4*>(qc + M) = make_uint4(w_hi[0], w_hi[1], w_hi[2], w_hi[3]);
+        if ((c & 1u) == 0u) {
+            const int64_t sbr = m0 / 32 + (c >> 1);
+            uint16_t sv = uint16_t(b_lo | (b_hi << 8));
+            if (kGrouped && sbr >= tail_br) sv = 0;
+            *reinterpret_cast<uint16_t*>(s_col + sbr * N + n0 + 2 * cp) = sv;
         }
     }
-    uint8_t* qc = q_col + (n0 + 2 * cp) * M + m0 + 32 * br;
-    *reinterpret_cast<uint4*>(qc) = make_uint4(w_lo[0], w_lo[1], w_lo[2], w_lo[3]);
-    *reinterpret_cast<uint4*>(qc + 16) = make_uint4(w_lo[4], w_lo[5], w_lo[6], w_lo[7]);
-    *reinterpret_cast<uint4*>(qc + M) = make_uint4(w_hi[0], w_hi[1], w_hi[2], w_hi[3]);
-    *reinterpret_cast<uint4*>(qc + M + 16) = make_uint4(w_hi[4], w_hi[5], w_hi[6], w_hi[7]);
-
-    const int64_t sbr = m0 / 32 + br;
-    uint16_t sv = uint16_t(b_lo | (b_hi << 8));
-    if (kGrouped && sbr >= tail_br) sv = 0;
-    *reinterpret_cast<uint16_t*>(s_col + sbr * N + n0 + 2 * cp) = sv;
 }
 
 __global__ __launch_bounds__(kThreads)

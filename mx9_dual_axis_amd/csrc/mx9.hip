@@ -7,8 +7,12 @@
 // -126); prime one bit per pair of elements, set when the pair lies wholly
 // below 2^E and uses the finer grid 2^(E-7).
 //
-// One thread per block of 16.  bf16 inputs are widened exactly to fp32 bit
-// patterns (bf16 is the upper half of binary32), so one code path serves
+// Contiguous inputs (row pitch == cols, cols % 16 == 0) take the flat
+// kernels: a block is split over 2 lanes (bf16) or 4 lanes (fp32) so that
+// every wave-wide load and store is one contiguous range, and the block's
+// exponent maximum and prime bits are combined with DPP.  Strided or ragged
+// inputs take one thread per block.  bf16 inputs are widened exactly to fp32
+// bit patterns (bf16 is the upper half of binary32), so one code path serves
 // both input types.  The quotient x / 2^(E-6-p) is formed with v_ldexp_f32,
 // exact because the divisor is a power of two and |quotient| < 2^8, then
 // rounded half-to-even by v_rndne_f32; fp32 denormals are kept (no flush),
@@ -146,6 +150,124 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// ---------------------------------------------------------------------------
+// Flat paths: the input is one contiguous run of nb blocks (ld == cols and
+// cols % 16 == 0).  A block is shared by L = 16 * esz / 16 lanes (2 for bf16,
+// 4 for fp32) that each hold one 16-byte piece, so every wave-wide load and
+// store covers a contiguous range.  The block's exponent maximum and its
+// prime bits are combined across the L lanes with DPP quad permutes.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
+    return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {
+    return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x4E, 0xF, 0xF, true));
+}
+
+// kDtype 0: fp32, 4 lanes x 4 elements per block.  1: bf16, 2 lanes x 8.
+template <int kDtype>
+__global__ __launch_bounds__(kThreads)
+void mx9_pack_flat(const void* __restrict__ xv, uint64_t nb, int8_t* __restrict__ q,
+                   uint8_t* __restrict__ max_exp, uint8_t* __restrict__ prime) {
+    constexpr int kLanes = kDtype == 0 ? 4 : 2;          // lanes per block
+    constexpr int kElems = 16 / kLanes;                   // elements per lane
+    constexpr int kLoads = kLanes;                        // 16-byte loads per lane per pass
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t part = lane % kLanes;                  // which piece of its block
+    // each wave owns 64 consecutive blocks: kLoads instructions of 1 KiB
+    const uint64_t wave_blk0 = (uint64_t(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6)) * 64;
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+        const uint64_t blk = wave_blk0 + uint64_t(k) * (64 / kLanes) + lane / kLanes;
+        const bool live = blk < nb;
+        uint32_t w[kElems];
+        if (live) {
+            const uint4 d = reinterpret_cast<const uint4*>(xv)[blk * kLanes + part];
+            if (kDtype == 0) {
+                w[0] = d.x; w[1] = d.y; w[2] = d.z; w[3] = d.w;
+            } else {
+                const uint32_t dd[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { w[2 * i] = dd[i] << 16; w[2 * i + 1] = dd[i] & 0xFFFF0000u; }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kElems; ++i) w[i] = 0u;
+        }
+        // exponent fields and the block maximum across the kLanes lanes
+        uint32_t ef[kElems];
+        uint32_t emax = 0;
+#pragma unroll
+        for (int i = 0; i < kElems; ++i) { ef[i] = efield(w[i]); emax = max(emax, ef[i]); }
+        emax = max(emax, dpp_xor1(emax));
+        if (kLanes == 4) emax = max(emax, dpp_xor2(emax));
+        const uint32_t S = max(emax, 1u);
+        uint32_t bits = 0, qlo = 0, qhi = 0;
+#pragma unroll
+        for (int j = 0; j < kElems / 2; ++j) {
+            const uint32_t p = max(ef[2 * j], ef[2 * j + 1]) < S ? 1u : 0u;
+            bits |= p << j;
+            const int shift = 133 + int(p) - int(S);
+            const uint32_t pair = qbyte(w[2 * j], shift) | (qbyte(w[2 * j + 1], shift) << 8);
+            if (j < 2) qlo |= pair << (16 * j);
+            else qhi |= pair << (16 * (j - 2));
+        }
+        // the block's prime byte: this lane's pairs sit at bit (kElems / 2) * part
+        uint32_t pr = bits << ((kElems / 2) * part);
+        pr |= dpp_xor1(pr);
+        if (kLanes == 4) pr |= dpp_xor2(pr);
+        if (emax == 255u) { qlo = 0u; qhi = 0u; pr = 0u; }
+        if (live) {
+            uint8_t* qb = reinterpret_cast<uint8_t*>(q) + blk * 16 + part * kElems;
+            if (kElems == 8) *reinterpret_cast<uint2*>(qb) = make_uint2(qlo, qhi);
+            else *reinterpret_cast<uint32_t*>(qb) = qlo;
+            if (part == 0) max_exp[blk] = uint8_t(emax == 255u ? 255u : S);
+            if (part == 1) prime[blk] = uint8_t(pr);
+        }
+    }
+}
+
+// kOut 0: fp32 output, 4 lanes x 4 elements per block.  1: bf16, 2 lanes x 8.
+template <int kOut>
+__global__ __launch_bounds__(kThreads)
+void mx9_unpack_flat(const int8_t* __restrict__ q, const uint8_t* __restrict__ max_exp,
+                     const uint8_t* __restrict__ prime, uint64_t nb, void* __restrict__ yv) {
+    constexpr int kLanes = kOut == 0 ? 4 : 2;
+    constexpr int kElems = 16 / kLanes;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t part = lane % kLanes;
+    const uint64_t wave_blk0 = (uint64_t(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6)) * 64;
+#pragma unroll
+    for (int k = 0; k < kLanes; ++k) {
+        const uint64_t blk = wave_blk0 + uint64_t(k) * (64 / kLanes) + lane / kLanes;
+        if (blk >= nb) continue;
+        const uint8_t* qb = reinterpret_cast<const uint8_t*>(q) + blk * 16 + part * kElems;
+        uint32_t qd[2];
+        if (kElems == 8) { const uint2 t2 = *reinterpret_cast<const uint2*>(qb); qd[0] = t2.x; qd[1] = t2.y; }
+        else { qd[0] = *reinterpret_cast<const uint32_t*>(qb); qd[1] = 0u; }
+        const uint32_t S = max_exp[blk];
+        const uint32_t pr = uint32_t(prime[blk]) >> ((kElems / 2) * part);
+        float y[kElems];
+#pragma unroll
+        for (int i = 0; i < kElems; ++i) {
+            const int qi = int(int8_t(uint8_t(qd[i >> 2] >> (8 * (i & 3)))));
+            const int p = int((pr >> (i >> 1)) & 1u);
+            y[i] = __builtin_ldexpf(float(qi), int(S) - 133 - p);
+        }
+        if (kOut == 0) {
+            float4 o = make_float4(y[0], y[1], y[2], y[3]);
+            if (S == 255u) o = make_float4(__uint_as_float(0x7FC00000u), __uint_as_float(0x7FC00000u),
+                                           __uint_as_float(0x7FC00000u), __uint_as_float(0x7FC00000u));
+            reinterpret_cast<float4*>(yv)[blk * 4 + part] = o;
+        } else {
+            uint4 o = make_uint4(bf16_pair(y[0], y[1]), bf16_pair(y[2], y[3]), bf16_pair(y[4], y[5]), bf16_pair(y[6], y[7]));
+            if (S == 255u) o = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+            reinterpret_cast<uint4*>(yv)[blk * 2 + part] = o;
+        }
+    }
+}
+
 template <int kOut, bool kVec>
 __global__ __launch_bounds__(kThreads)
 void mx9_unpack_kernel(const int8_t* __restrict__ q, const uint8_t* __restrict__ max_exp,
@@ -202,6 +324,13 @@ hipError_t launch_mx9_pack(const void* x, int dtype, int64_t rows, int64_t cols,
     const uint64_t nb = uint64_t(rows) * bpr;
     const dim3 grid(uint32_t((nb + kThreads - 1) / kThreads));
     const bool vec = cols % 16 == 0 && aligned16(x) && (ld_x * esz) % 16 == 0;
+    if (vec && ld_x == cols && aligned16(q)) {
+        // 64 blocks per wave, 4 waves per workgroup
+        const dim3 fgrid(uint32_t((nb + 255) / 256));
+        if (dtype == 0) hipLaunchKernelGGL(mx9_pack_flat<0>, fgrid, dim3(kThreads), 0, stream, x, nb, q, max_exp, prime);
+        else hipLaunchKernelGGL(mx9_pack_flat<1>, fgrid, dim3(kThreads), 0, stream, x, nb, q, max_exp, prime);
+        return hipGetLastError();
+    }
     if (dtype == 0) {
         if (vec) hipLaunchKernelGGL(mx9_pack_vec<0>, grid, dim3(kThreads), 0, stream, x, ld_x, bpr, nb, q, max_exp, prime);
         else hipLaunchKernelGGL(mx9_pack_any<0>, grid, dim3(kThreads), 0, stream, x, ld_x, cols, bpr, nb, q, max_exp, prime);
@@ -220,6 +349,12 @@ hipError_t launch_mx9_unpack(const int8_t* q, const uint8_t* max_exp, const uint
     const uint64_t nb = uint64_t(rows) * bpr;
     const dim3 grid(uint32_t((nb + kThreads - 1) / kThreads));
     const bool vec = cols % 16 == 0 && aligned16(y) && (ld_y * esz) % 16 == 0;
+    if (vec && ld_y == cols && aligned16(q)) {
+        const dim3 fgrid(uint32_t((nb + 255) / 256));
+        if (out_dtype == 0) hipLaunchKernelGGL(mx9_unpack_flat<0>, fgrid, dim3(kThreads), 0, stream, q, max_exp, prime, nb, y);
+        else hipLaunchKernelGGL(mx9_unpack_flat<1>, fgrid, dim3(kThreads), 0, stream, q, max_exp, prime, nb, y);
+        return hipGetLastError();
+    }
     if (out_dtype == 0) {
         if (vec) hipLaunchKernelGGL((mx9_unpack_kernel<0, true>), grid, dim3(kThreads), 0, stream, q, max_exp, prime, cols, bpr, nb, y, ld_y);
         else hipLaunchKernelGGL((mx9_unpack_kernel<0, false>), grid, dim3(kThreads), 0, stream, q, max_exp, prime, cols, bpr, nb, y, ld_y);

@@ -71,10 +71,12 @@ enum { MX_OFFS_OK = 0, MX_OFFS_ORDER = 1, MX_OFFS_ALIGN = 2, MX_OFFS_BOUNDS = 3 
  * on both axes.  Inf (no NaN): rowwise scale 255 with 0x7F codes; colwise
  * scale 254 with +-Inf -> +-448 and the other elements scaled by 2^-127.
  *
- * Errors: MX_E_NULL (a pointer NULL while M, N > 0), MX_E_BLOCK, MX_E_MODE, MX_E_SHAPE
- * (M or N negative, not a multiple of 128, or above 2^30), MX_E_STRIDE
- * (ld_x < N or ld_x not a multiple of 8), MX_E_ALIGN (any pointer not
- * 16-byte aligned), MX_E_OVERLAP.  M == 0 or N == 0 is a no-op.
+ * Errors: MX_E_NULL (a pointer NULL while M, N > 0), MX_E_BLOCK, MX_E_MODE,
+ * MX_E_SHAPE (M or N negative, not a multiple of 128, or above 2^24),
+ * MX_E_STRIDE (ld_x < N, not a multiple of 8, or above 2^24), MX_E_ALIGN
+ * (any pointer not 16-byte aligned), MX_E_OVERLAP.  M == 0 or N == 0 is a
+ * no-op.  The call may enqueue two kernels on the stream; s_row is complete
+ * once both have run.
  */
 int mx_quantize_2d_dual(const uint16_t *x, int64_t M, int64_t N, int64_t ld_x,
                         int32_t block_size, int32_t scaling_mode,

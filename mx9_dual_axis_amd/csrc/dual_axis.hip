@@ -34,6 +34,15 @@
 //              spreads the concurrently active row segments of the input and
 //              of both outputs over the HBM channels better than row-major or
 //              column-major order (measured).
+//   * s_row  : a tile owns only 4 scale bytes per row, and 128 scattered 4-byte
+//              stores per tile cost more than the rest of the tile's writes.
+//              When N <= 16256 and N % 512 == 0, each tile instead writes its
+//              512 scale bytes as one contiguous run inside its band's s_row
+//              rows (a band's rows are one contiguous range), and a second,
+//              small kernel transposes each band in place through LDS.
+//   * offsets: per-tile base pointers are uniform and per-lane offsets are
+//              32-bit, which the host guarantees by limiting M, N and the row
+//              pitch to 2^24.
 #include "mxq_kernels.h"
 
 #include <limits.h>
@@ -43,6 +52,7 @@ namespace {
 
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
+constexpr int64_t kMaxStagedN = 16256;   // 127 tiles x 129 dwords = 65,532 bytes of LDS
 
 typedef short v2i16 __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
@@ -114,7 +124,7 @@ __device__ void validate_offsets(const int32_t* offs, int32_t G, int64_t M, int3
     if (threadIdx.x == 0) *err = first_bad == INT_MAX ? 0 : offs_code(offs, first_bad, M);
 }
 
-template <bool kGrouped>
+template <bool kGrouped, bool kStage>
 __global__ __launch_bounds__(kThreads)
 void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, int64_t N,
                       uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
@@ -173,8 +183,16 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
     }
     __syncthreads();
 
-    if (t < kTile)
+    if (kStage) {
+        // Sector-complete staging: the 8 tiles of a group share the 128 x 32-byte
+        // s_row region of their rows; tile jt writes its 512 bytes as pieces
+        // 16*jt .. 16*jt+15 (piece P = the region's row P, 8 of this tile's rows
+        // per piece).  A second pass puts every piece into final row order.
+        if (t < 32)
+            *reinterpret_cast<uint4*>(s_row + m0 * (N / 32) + int64_t(tn) * 512 + 16 * t) = reinterpret_cast<const uint4*>(lds_srow)[t];
+    } else if (t < kTile) {
         *reinterpret_cast<uint32_t*>(s_row + (m0 + t) * (N / 32) + n0 / 32) = lds_srow[t];
+    }
 
     // ---- colwise 32x1 pass ----
     // Unit = (column pair cp, 16-row chunk c); each thread takes two units.
@@ -227,6 +245,39 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
     }
 }
 
+// Second pass of the staged s_row layout.  The main kernel writes each
+// tile's 128 rows x 4 scale bytes as one contiguous 512-byte run at offset
+// 512 * tn inside its band's s_row rows (a band's 128 rows of s_row are one
+// contiguous 4N-byte range), i.e. the band holds a [tiles_n][128] array of
+// dwords.  Here one workgroup per band reads the whole range into LDS and
+// writes it back transposed to the final [128][tiles_n] row layout.
+constexpr int kPermThreads = 1024;
+
+__global__ __launch_bounds__(kPermThreads)
+void srow_permute_kernel(uint8_t* __restrict__ s_row, int64_t N) {
+    extern __shared__ uint32_t lds_band[];               // [tiles_n][129] dwords
+    const uint32_t tiles_n = uint32_t(N / kTile);
+    const uint32_t nq = tiles_n * 32;                     // 16-byte chunks in the band
+    uint8_t* band = s_row + int64_t(blockIdx.x) * kTile * (N / 32);
+    for (uint32_t i = threadIdx.x; i < nq; i += kPermThreads) {
+        const uint4 v = reinterpret_cast<const uint4*>(band)[i];
+        const uint32_t tn = i >> 5, r = (i & 31u) * 4u;   // 32 chunks per tile
+        uint32_t* d = lds_band + tn * 129u + r;
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < nq; i += kPermThreads) {
+        const uint32_t f = i * 4u;                        // first final dword of this chunk
+        const uint32_t r = f / tiles_n, tn = f - r * tiles_n;
+        uint4 v;
+        v.x = lds_band[(tn + 0) * 129u + r];
+        v.y = lds_band[(tn + 1) * 129u + r];
+        v.z = lds_band[(tn + 2) * 129u + r];
+        v.w = lds_band[(tn + 3) * 129u + r];
+        reinterpret_cast<uint4*>(band)[i] = v;
+    }
+}
+
 __global__ __launch_bounds__(kThreads)
 void offs_validate_kernel(const int32_t* __restrict__ offs, int32_t G, int64_t M, int32_t* __restrict__ err) {
     validate_offsets(offs, G, M, err);
@@ -240,13 +291,26 @@ hipError_t launch_dual_axis(const uint16_t* x, int64_t M, int64_t N, int64_t ld_
                             hipStream_t stream) {
     const uint32_t tiles_n = uint32_t(N / kTile);
     const uint32_t tiles = uint32_t((M / kTile) * (N / kTile));
-    if (grouped)
-        hipLaunchKernelGGL(dual_axis_kernel<true>, dim3(tiles), dim3(kThreads), 0, stream,
+    // the band fits the permute pass's LDS, and its chunks hold 4 whole tiles
+    const bool stage = N <= kMaxStagedN && N % 512 == 0;
+    const int32_t* no_offs = nullptr;
+    int32_t* no_err = nullptr;
+    if (grouped && stage)
+        hipLaunchKernelGGL((dual_axis_kernel<true, true>), dim3(tiles), dim3(kThreads), 0, stream,
                            x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles, offs, G, err);
+    else if (grouped)
+        hipLaunchKernelGGL((dual_axis_kernel<true, false>), dim3(tiles), dim3(kThreads), 0, stream,
+                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles, offs, G, err);
+    else if (stage)
+        hipLaunchKernelGGL((dual_axis_kernel<false, true>), dim3(tiles), dim3(kThreads), 0, stream,
+                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles, no_offs, 0, no_err);
     else
-        hipLaunchKernelGGL(dual_axis_kernel<false>, dim3(tiles), dim3(kThreads), 0, stream,
-                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles,
-                           static_cast<const int32_t*>(nullptr), 0, static_cast<int32_t*>(nullptr));
+        hipLaunchKernelGGL((dual_axis_kernel<false, false>), dim3(tiles), dim3(kThreads), 0, stream,
+                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles, no_offs, 0, no_err);
+    if (stage) {
+        const uint32_t lds = uint32_t(N / kTile) * 129u * 4u;
+        hipLaunchKernelGGL(srow_permute_kernel, dim3(uint32_t(M / kTile)), dim3(kPermThreads), lds, stream, s_row, N);
+    }
     return hipGetLastError();
 }
 

@@ -26,43 +26,72 @@ constexpr int kThreads = 256;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t efield(uint32_t w) { return (w >> 23) & 0xFFu; }
 
-__device__ __forceinline__ uint32_t qbyte(uint32_t w, int shift) {
-    int q = int(__builtin_rintf(__builtin_ldexpf(__uint_as_float(w), shift)));
-    q = q < -127 ? -127 : (q > 127 ? 127 : q);
-    return uint32_t(q) & 0xFFu;
+// round-half-even(x * 2^shift) clamped to [-127, 127], returned in the low
+// byte of the result (two's complement).  |x * 2^shift| < 2^8 for every
+// element of a block, and ldexp is exact there.  Clamping to +-127 before
+// rounding equals clamping after (the bounds are integers).  Adding 1.5*2^23
+// rounds half-to-even to an integer held in the low mantissa bits, whose low
+// byte is the two's-complement int8 of the rounded value.
+__device__ __forceinline__ uint32_t qbits(uint32_t w, int shift) {
+    float t = __builtin_ldexpf(__uint_as_float(w), shift);
+    t = __builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
+    return __float_as_uint(t + 12582912.0f);
+}
+
+// Low bytes of four qbits results -> one dword, element a in byte 0.
+__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
+// Quantize pairs of fp32 patterns against the block's shared exponent byte S.
+// A pair is demoted (p = 1) when its larger magnitude is below 2^(S-127),
+// i.e. when its larger magnitude pattern is below S << 23 (magnitudes and
+// their bit patterns order alike).  Returns the q bytes of kPairs pairs in
+// kPairs / 2 dwords and the pair bits in *bits (LSB = first pair).
+template <int kPairs>
+__device__ __forceinline__ void quantize_pairs(const uint32_t (&w)[2 * kPairs], uint32_t S,
+                                               uint32_t (&qd)[kPairs / 2], uint32_t& bits) {
+    uint32_t qb[2 * kPairs];
+    bits = 0;
+#pragma unroll
+    for (int j = 0; j < kPairs; ++j) {
+        const uint32_t pm = max(w[2 * j] & 0x7FFFFFFFu, w[2 * j + 1] & 0x7FFFFFFFu);
+        const uint32_t p = pm < (S << 23) ? 1u : 0u;
+        bits |= p << j;
+        const int shift = 133 + int(p) - int(S);          // 6 + p - E, E = S - 127
+        qb[2 * j] = qbits(w[2 * j], shift);
+        qb[2 * j + 1] = qbits(w[2 * j + 1], shift);
+    }
+#pragma unroll
+    for (int k = 0; k < kPairs / 2; ++k) qd[k] = pack4(qb[4 * k], qb[4 * k + 1], qb[4 * k + 2], qb[4 * k + 3]);
+}
+
+// Largest magnitude pattern of n fp32 patterns (NaN > Inf > finite).
+template <int kN>
+__device__ __forceinline__ uint32_t max_magnitude(const uint32_t (&w)[kN]) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < kN; ++i) m = max(m, w[i] & 0x7FFFFFFFu);
+    return m;
 }
 
 // Pack 16 fp32 patterns: q bytes (4 dwords), max_exp byte, prime byte.
+// The shared exponent byte is the largest exponent field raised to >= 1;
+// an Inf or NaN (exponent field 255) poisons the block.
 __device__ __forceinline__ void pack16(const uint32_t (&w)[16], uint32_t (&qd)[4], uint32_t& me,
                                        uint32_t& pr) {
-    uint32_t ef[16];
-    uint32_t emax = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        ef[i] = efield(w[i]);
-        emax = max(emax, ef[i]);
-    }
-    if (emax == 255u) {                 // Inf or NaN: poisoned block
+    const uint32_t mmax = max_magnitude(w);
+    const uint32_t S = max(mmax >> 23, 1u);
+    quantize_pairs<8>(w, S, qd, pr);
+    me = S;
+    if (mmax >= 0x7F800000u) {          // Inf or NaN: poisoned block
         qd[0] = qd[1] = qd[2] = qd[3] = 0u;
         me = 255u;
         pr = 0u;
-        return;
     }
-    const uint32_t S = max(emax, 1u);
-    uint32_t bits = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t p = max(ef[2 * j], ef[2 * j + 1]) < S ? 1u : 0u;
-        bits |= p << j;
-        const int shift = 133 + int(p) - int(S);          // 6 + p - E, E = S - 127
-        const uint32_t pair = qbyte(w[2 * j], shift) | (qbyte(w[2 * j + 1], shift) << 8);
-        if (j & 1) qd[j >> 1] |= pair << 16;
-        else qd[j >> 1] = pair;
-    }
-    me = S;
-    pr = bits;
 }
 
 // Vector path: cols % 16 == 0 and 16-byte aligned block starts.
@@ -165,67 +194,58 @@ __device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {
     return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x4E, 0xF, 0xF, true));
 }
 
+// One pass of the flat pack: this lane's 16-byte piece of block blk.
+template <int kDtype, bool kGuard>
+__device__ __forceinline__ void pack_piece(const void* __restrict__ xv, uint64_t nb, uint64_t blk,
+                                           uint32_t part, int8_t* __restrict__ q,
+                                           uint8_t* __restrict__ max_exp, uint8_t* __restrict__ prime) {
+    constexpr int kLanes = kDtype == 0 ? 4 : 2;          // lanes per block
+    constexpr int kElems = 16 / kLanes;                   // elements per lane
+    const bool live = !kGuard || blk < nb;
+    uint32_t w[kElems];
+    uint4 d = make_uint4(0u, 0u, 0u, 0u);
+    if (live) d = reinterpret_cast<const uint4*>(xv)[blk * kLanes + part];
+    if (kDtype == 0) {
+        w[0] = d.x; w[1] = d.y; w[2] = d.z; w[3] = d.w;
+    } else {
+        const uint32_t dd[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { w[2 * i] = dd[i] << 16; w[2 * i + 1] = dd[i] & 0xFFFF0000u; }
+    }
+    uint32_t mmax = max_magnitude(w);
+    mmax = max(mmax, dpp_xor1(mmax));
+    if (kLanes == 4) mmax = max(mmax, dpp_xor2(mmax));
+    const uint32_t S = max(mmax >> 23, 1u);
+    uint32_t qd[kElems / 4], bits;
+    quantize_pairs<kElems / 2>(w, S, qd, bits);
+    // the block's prime byte: this lane's pairs start at bit (kElems / 2) * part
+    uint32_t pr = bits << ((kElems / 2) * part);
+    pr |= dpp_xor1(pr);
+    if (kLanes == 4) pr |= dpp_xor2(pr);
+    const bool poison = mmax >= 0x7F800000u;
+    if (live) {
+        uint8_t* qb = reinterpret_cast<uint8_t*>(q) + blk * 16 + part * kElems;
+        if (kElems == 8) *reinterpret_cast<uint2*>(qb) = poison ? make_uint2(0u, 0u) : make_uint2(qd[0], qd[1]);
+        else *reinterpret_cast<uint32_t*>(qb) = poison ? 0u : qd[0];
+        if (part == 0) max_exp[blk] = uint8_t(poison ? 255u : S);
+        if (part == 1) prime[blk] = uint8_t(poison ? 0u : pr);
+    }
+}
+
 // kDtype 0: fp32, 4 lanes x 4 elements per block.  1: bf16, 2 lanes x 8.
+// Each wave owns 64 / kLanes consecutive blocks: one contiguous 1 KiB load.
 template <int kDtype>
 __global__ __launch_bounds__(kThreads)
 void mx9_pack_flat(const void* __restrict__ xv, uint64_t nb, int8_t* __restrict__ q,
                    uint8_t* __restrict__ max_exp, uint8_t* __restrict__ prime) {
-    constexpr int kLanes = kDtype == 0 ? 4 : 2;          // lanes per block
-    constexpr int kElems = 16 / kLanes;                   // elements per lane
-    constexpr int kLoads = kLanes;                        // 16-byte loads per lane per pass
+    constexpr int kLanes = kDtype == 0 ? 4 : 2;
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t part = lane % kLanes;                  // which piece of its block
-    // each wave owns 64 consecutive blocks: kLoads instructions of 1 KiB
-    const uint64_t wave_blk0 = (uint64_t(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6)) * 64;
-#pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-        const uint64_t blk = wave_blk0 + uint64_t(k) * (64 / kLanes) + lane / kLanes;
-        const bool live = blk < nb;
-        uint32_t w[kElems];
-        if (live) {
-            const uint4 d = reinterpret_cast<const uint4*>(xv)[blk * kLanes + part];
-            if (kDtype == 0) {
-                w[0] = d.x; w[1] = d.y; w[2] = d.z; w[3] = d.w;
-            } else {
-                const uint32_t dd[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) { w[2 * i] = dd[i] << 16; w[2 * i + 1] = dd[i] & 0xFFFF0000u; }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < kElems; ++i) w[i] = 0u;
-        }
-        // exponent fields and the block maximum across the kLanes lanes
-        uint32_t ef[kElems];
-        uint32_t emax = 0;
-#pragma unroll
-        for (int i = 0; i < kElems; ++i) { ef[i] = efield(w[i]); emax = max(emax, ef[i]); }
-        emax = max(emax, dpp_xor1(emax));
-        if (kLanes == 4) emax = max(emax, dpp_xor2(emax));
-        const uint32_t S = max(emax, 1u);
-        uint32_t bits = 0, qlo = 0, qhi = 0;
-#pragma unroll
-        for (int j = 0; j < kElems / 2; ++j) {
-            const uint32_t p = max(ef[2 * j], ef[2 * j + 1]) < S ? 1u : 0u;
-            bits |= p << j;
-            const int shift = 133 + int(p) - int(S);
-            const uint32_t pair = qbyte(w[2 * j], shift) | (qbyte(w[2 * j + 1], shift) << 8);
-            if (j < 2) qlo |= pair << (16 * j);
-            else qhi |= pair << (16 * (j - 2));
-        }
-        // the block's prime byte: this lane's pairs sit at bit (kElems / 2) * part
-        uint32_t pr = bits << ((kElems / 2) * part);
-        pr |= dpp_xor1(pr);
-        if (kLanes == 4) pr |= dpp_xor2(pr);
-        if (emax == 255u) { qlo = 0u; qhi = 0u; pr = 0u; }
-        if (live) {
-            uint8_t* qb = reinterpret_cast<uint8_t*>(q) + blk * 16 + part * kElems;
-            if (kElems == 8) *reinterpret_cast<uint2*>(qb) = make_uint2(qlo, qhi);
-            else *reinterpret_cast<uint32_t*>(qb) = qlo;
-            if (part == 0) max_exp[blk] = uint8_t(emax == 255u ? 255u : S);
-            if (part == 1) prime[blk] = uint8_t(pr);
-        }
-    }
+    const uint32_t part = lane % kLanes;
+    const uint64_t wave_blk0 = (uint64_t(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6)) * (64 / kLanes);
+    if (wave_blk0 + 64 / kLanes <= nb)
+        pack_piece<kDtype, false>(xv, nb, wave_blk0 + lane / kLanes, part, q, max_exp, prime);
+    else
+        pack_piece<kDtype, true>(xv, nb, wave_blk0 + lane / kLanes, part, q, max_exp, prime);
 }
 
 // kOut 0: fp32 output, 4 lanes x 4 elements per block.  1: bf16, 2 lanes x 8.
@@ -325,8 +345,8 @@ hipError_t launch_mx9_pack(const void* x, int dtype, int64_t rows, int64_t cols,
     const dim3 grid(uint32_t((nb + kThreads - 1) / kThreads));
     const bool vec = cols % 16 == 0 && aligned16(x) && (ld_x * esz) % 16 == 0;
     if (vec && ld_x == cols && aligned16(q)) {
-        // 64 blocks per wave, 4 waves per workgroup
-        const dim3 fgrid(uint32_t((nb + 255) / 256));
+        // 64 / kLanes blocks per wave, 4 waves per workgroup
+        const dim3 fgrid(uint32_t((nb + (dtype == 0 ? 63 : 127)) / (dtype == 0 ? 64 : 128)));
         if (dtype == 0) hipLaunchKernelGGL(mx9_pack_flat<0>, fgrid, dim3(kThreads), 0, stream, x, nb, q, max_exp, prime);
         else hipLaunchKernelGGL(mx9_pack_flat<1>, fgrid, dim3(kThreads), 0, stream, x, nb, q, max_exp, prime);
         return hipGetLastError();

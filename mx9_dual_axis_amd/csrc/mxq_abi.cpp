@@ -15,6 +15,7 @@
 namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxDual = int64_t(1) << 24;   // dual-axis: 32-bit per-lane offsets within a tile
 constexpr uint64_t kMaxThreads = 0xFFFFFFFFull - 256;   // grid.x * block.x must fit 32 bits
 
 struct Span {
@@ -50,10 +51,10 @@ int check_dual(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x, int32_t bl
     if (!empty && (!x || !q_row || !s_row || !q_col || !s_col)) return MX_E_NULL;
     if (block_size != 32) return MX_E_BLOCK;
     if (scaling_mode != MX_SCALE_RCEIL) return MX_E_MODE;
-    if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim || M % 128 != 0 || N % 128 != 0)
+    if (M < 0 || N < 0 || M > kMaxDual || N > kMaxDual || M % 128 != 0 || N % 128 != 0)
         return MX_E_SHAPE;
     if (uint64_t(M / 128) * uint64_t(N / 128) * 256 > kMaxThreads) return MX_E_SHAPE;
-    if (ld_x < N || ld_x % 8 != 0 || ld_x > (int64_t(1) << 40)) return MX_E_STRIDE;
+    if (ld_x < N || ld_x % 8 != 0 || ld_x > kMaxDual) return MX_E_STRIDE;
     if (!empty && (!aligned(x, 16) || !aligned(q_row, 16) || !aligned(s_row, 16) ||
                    !aligned(q_col, 16) || !aligned(s_col, 16)))
         return MX_E_ALIGN;

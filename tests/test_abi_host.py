@@ -56,7 +56,8 @@ def test_dual_validation_codes():
     assert _dual(bs=16) == 3
     assert _dual(mode=1) == 4
     assert _dual(M=200) == 5 and _dual(N=100) == 5 and _dual(M=-128) == 5
-    assert _dual(M=1 << 31) == 5
+    assert _dual(M=1 << 31) == 5 and _dual(N=(1 << 24) + 128, ld=(1 << 24) + 128) == 5
+    assert _dual(ld=(1 << 24) + 8) == 6
     assert _dual(ld=128) == 6 and _dual(ld=260) == 6
     assert _dual(qc=FAKE * 4 + 8) == 7
     assert _dual(qc=FAKE * 2 + 4096) == 8            # q_col starts inside q_row

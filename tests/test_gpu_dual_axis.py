@@ -49,6 +49,22 @@ def test_dense_parity(M, N, kind, seed):
     _assert_equal(out, oracle.mxfp8_dual(xb, threads=THREADS), f"{M}x{N} {kind}")
 
 
+@pytest.mark.parametrize("M,N", [
+    (128, 15872),    # the widest shape whose rowwise scales go through the band transpose
+    (256, 16384),    # wider: rowwise scales written directly
+    (384, 2560),     # N % 512 == 0, staged
+    (128, 1152),     # N % 512 != 0, direct
+])
+def test_rowwise_scale_paths(M, N):
+    dev = require_gpu()
+    say(f"s_row paths M={M} N={N}")
+    xb = synth.mixed_rows(M, N, M + N)
+    out = _dirty_outputs(M, N, dev)
+    mxq.mx_quantize_2d_dual(bf16_to_dev(xb), out=out)
+    torch.cuda.synchronize()
+    _assert_equal(out, oracle.mxfp8_dual(xb, threads=THREADS), f"{M}x{N}")
+
+
 def test_dense_strided_input():
     """Row pitch larger than N (a column slice of a wider matrix)."""
     dev = require_gpu()

@@ -133,6 +133,39 @@ def test_strided_and_unaligned_inputs():
     assert (got[:, 256:] == 7.0).all()
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_every_kernel_path(dtype):
+    """Flat (contiguous), vector (strided, 16-byte aligned rows) and general
+    (unaligned or ragged) kernels of pack and unpack, for both dtypes."""
+    dev = require_gpu()
+    say(f"mx9 kernel paths {dtype}")
+    wide = synth.mx9_weights(40, 512, 21, dtype)
+    esz = 4 if dtype == "fp32" else 2
+    cases = {
+        "flat": (wide[:, :256], _to_dev(np.ascontiguousarray(wide[:, :256]))),
+        "vector": (wide[:, 128:384], _to_dev(wide)[:, 128:384]),          # ld 512, aligned rows
+        "general": (wide[:, 3:203], _to_dev(wide)[:, 3:203]),             # unaligned, ragged
+    }
+    for name, (host_x, dev_x) in cases.items():
+        rows, cols = host_x.shape
+        if name == "vector":
+            assert dev_x.stride(0) * esz % 16 == 0 and dev_x.data_ptr() % 16 == 0
+        q, e, p, _ = _check_pack(np.ascontiguousarray(host_x), f"{dtype} {name}", dev_x=dev_x)
+        for od, td in (("fp32", torch.float32), ("bf16", torch.bfloat16)):
+            want = oracle.mx9_unpack(host(q), host(e), host(p), rows, cols, od)
+            # contiguous output (flat), wider aligned output (vector), odd pitch (general)
+            for pitch in (cols, cols + 64, cols + 3):
+                y = torch.full((rows, pitch), 5, dtype=td, device=dev)
+                mxq.mx9_unpack(q, e, p, rows, cols, out=y)
+                torch.cuda.synchronize()
+                got = host(y)[:, :cols]
+                gb = got.view(np.uint32) if od == "fp32" else got
+                wb = want.view(np.uint32) if od == "fp32" else want
+                assert np.array_equal(gb, wb), (dtype, name, od, pitch)
+                if pitch > cols:
+                    assert bool((y[:, cols:].float() == 5).all()), (dtype, name, od, pitch)
+
+
 def test_rejections_and_empty():
     dev = require_gpu()
     say("mx9 rejections")

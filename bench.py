@@ -8,10 +8,12 @@ then MX9 unpack back to bf16.  Inputs are resident in HBM before timing.
 
 Prints ONE JSON line.  ``value`` is the step's algorithmic bytes (what the
 method must read and write, per kernel) divided by the step time, in GB/s.
-``roofline`` describes the dominant kernel (the dual-axis cast): its
-algorithmic bytes per launch over its average launch time from HIP events on
-the launch stream, against MI355X's 8 TB/s HBM peak.  ``traffic`` is the HBM
-byte count per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+``roofline`` describes the dominant operation, the dual-axis cast: its
+algorithmic bytes per call over its average call time from HIP events on the
+launch stream (the call is the main kernel plus, for N <= 16256 with
+N % 512 == 0, the small kernel that transposes the staged rowwise scales),
+against MI355X's 8 TB/s HBM peak.  ``traffic`` is the HBM byte count per
+call (both kernels) from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
 summary, reported only while the kernel source matches the source those
 counters were taken on.  ``cpu_baseline`` times the CPU oracle on a bounded
 sample of the same workload.
@@ -180,7 +182,8 @@ def main():
                    "step_algorithmic_bytes": int(step_bytes)},
         "roofline": {"bound": "hbm", "achieved": dual["GB_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(dual["GB_s"] / PEAK_HBM_GBS, 4), "traffic": committed_traffic(),
-                     "kernel": "dual_axis_kernel<false>", "algorithmic_bytes_per_launch": dual["bytes"],
+                     "kernel": "dual_axis_kernel<false,true> + srow_permute_kernel (one dual-axis call)",
+                     "algorithmic_bytes_per_launch": dual["bytes"],
                      "avg_launch_us": dual["us"]},
         "kernels": kernels,
         "copy_GB_s": round(copy_gbs, 1),

@@ -16,9 +16,17 @@ against MI355X's 8 TB/s HBM peak.  ``traffic`` is the HBM byte count per
 call (both kernels) from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
 summary, reported only while the kernel source matches the source those
 counters were taken on.  ``cpu_baseline`` times the CPU oracle on a bounded
-sample of the same workload.
+sample of the same workload (a multithreaded leg of about ten seconds and a
+single-thread leg).
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--skip-cpu]
+``configs`` holds the other workloads, each timed per call with HIP events
+while rotating three input/output buffer sets so that MI355X's 256 MB
+last-level cache cannot serve a call from the previous one: the dense cast of
+the mixed-magnitude bf16 [8192, 7168] matrix, the grouped cast of bf16
+[16384, 5120] with 64 groups, and MX9 pack/unpack of the fp32 and bf16
+[4096, 14336] weights.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--skip-cpu] [--skip-configs]
 """
 from __future__ import annotations
 
@@ -63,20 +71,121 @@ def committed_traffic():
     return float(m_b.group(1))
 
 
-def cpu_baseline(xb, threads: int, rows: int):
-    """The oracle, as it stands, on the first `rows` rows of the workload:
-    dual-axis cast + MX9 pack + MX9 unpack (bf16)."""
+def cpu_baseline(xb, threads: int, budget_s: float, single_rows: int):
+    """The oracle, as it stands, on leading rows of the workload: dual-axis
+    cast + MX9 pack + MX9 unpack (bf16).  The multithreaded leg processes
+    chunks of 256 rows until ``budget_s`` seconds have passed; the
+    single-thread leg processes ``single_rows`` rows."""
     import oracle
-    sample = xb[:rows]
+    per_row = N * (DUAL_BYTES_PER_ELEM + PACK_BF16_BYTES_PER_ELEM + UNPACK_BF16_BYTES_PER_ELEM)
+
+    def run(rows_slice, nthreads):
+        oracle.mxfp8_dual(rows_slice, threads=nthreads)
+        q, e, p = oracle.mx9_pack(rows_slice, threads=nthreads)
+        oracle.mx9_unpack(q, e, p, rows_slice.shape[0], N, "bf16", threads=nthreads)
+
+    chunk, rows, busy = 256, 0, 0.0
+    while busy < budget_s and rows + chunk <= xb.shape[0]:
+        t0 = time.perf_counter()
+        run(xb[rows:rows + chunk], threads)
+        busy += time.perf_counter() - t0
+        rows += chunk
     t0 = time.perf_counter()
-    oracle.mxfp8_dual(sample, threads=threads)
-    q, e, p = oracle.mx9_pack(sample, threads=threads)
-    oracle.mx9_unpack(q, e, p, rows, N, "bf16", threads=threads)
-    dt = time.perf_counter() - t0
-    nbytes = rows * N * (DUAL_BYTES_PER_ELEM + PACK_BF16_BYTES_PER_ELEM + UNPACK_BF16_BYTES_PER_ELEM)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    run(xb[:single_rows], 1)
+    one = time.perf_counter() - t0
+    return {"value": round(rows * per_row / busy / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"first {rows} of {M} rows ({rows * N} elements) of the stress workload, "
-                      f"dual-axis cast + MX9 pack + unpack, {dt:.1f} s wall on {threads} threads"}
+                      f"dual-axis cast + MX9 pack + unpack, {busy:.1f} s on {threads} threads",
+            "single_thread": {"value": round(single_rows * per_row / one / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"first {single_rows} rows, same operations, {one:.1f} s"}}
+
+
+def time_rotating(calls, launches: int):
+    """Per-call durations (seconds, from HIP events on the launch stream) of
+    `launches` calls cycling through `calls` (one per buffer set)."""
+    import torch
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        calls[i % len(calls)]()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e-3 for a, b in evs]
+
+
+def summarize(ts, nbytes):
+    ts = sorted(ts)
+    med = ts[len(ts) // 2]
+    mean = sum(ts) / len(ts)
+    return {"us": round(mean * 1e6, 2), "median_us": round(med * 1e6, 2), "bytes": int(nbytes),
+            "GB_s": round(nbytes / mean / 1e9, 1), "frac": round(nbytes / mean / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def measure_configs(dev, launches: int, sets: int = 3):
+    """The other workloads, each over `sets` rotating buffer sets."""
+    import numpy as np
+    import torch
+
+    import mx9_dual_axis_amd as mxq
+    from mx9_dual_axis_amd import synth
+
+    def dev_bf16(xb):
+        return torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    u8 = dict(dtype=torch.uint8, device=dev)
+    res = {}
+
+    def dual_sets(xb, offs=None):
+        Mc, Nc = xb.shape
+        x0 = dev_bf16(xb)
+        xs = [x0] + [x0.clone() for _ in range(sets - 1)]
+        outs = [(torch.empty((Mc, Nc), **u8), torch.empty((Mc, Nc // 32), **u8),
+                 torch.empty((Nc, Mc), **u8), torch.empty((Mc // 32, Nc), **u8)) for _ in range(sets)]
+        if offs is None:
+            return [lambda x=x, o=o: mxq.mx_quantize_2d_dual(x, out=o) for x, o in zip(xs, outs)]
+        od = torch.from_numpy(offs).to(dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        return [lambda x=x, o=o: mxq.mx_quantize_grouped(x, od, err=err, out=o) for x, o in zip(xs, outs)]
+
+    print("bench: dense cast, mixed bf16 [8192, 7168]", file=sys.stderr, flush=True)
+    xb = synth.dual_mixed()
+    calls = dual_sets(xb)
+    res["dual_mixed"] = dict(workload="dense dual-axis cast, mixed-magnitude bf16 [8192, 7168]",
+                             **summarize(time_rotating(calls, launches), xb.size * DUAL_BYTES_PER_ELEM))
+    del calls
+
+    print("bench: grouped cast, bf16 [16384, 5120], 64 groups", file=sys.stderr, flush=True)
+    xb, offs = synth.grouped()
+    calls = dual_sets(xb, offs)
+    res["grouped"] = dict(workload="grouped dual-axis cast, bf16 [16384, 5120], 64 groups, offs[-1] = "
+                                   f"{int(offs[-1])}",
+                          **summarize(time_rotating(calls, launches), xb.size * DUAL_BYTES_PER_ELEM + 4 * offs.size))
+    del calls
+
+    print("bench: MX9 pack/unpack, weights [4096, 14336] fp32 and bf16", file=sys.stderr, flush=True)
+    w32 = synth.mx9_weights(4096, 14336, 4, "fp32")
+    rows, cols = w32.shape
+    nb = rows * cols // 16
+    for name, host_x, tdt, in_b in (("fp32", w32, torch.float32, 4), ("bf16", synth.to_bf16_bits(w32),
+                                                                      torch.bfloat16, 2)):
+        x0 = (torch.from_numpy(host_x).to(dev) if name == "fp32" else dev_bf16(host_x))
+        xs = [x0] + [x0.clone() for _ in range(sets - 1)]
+        packs = [(torch.empty((nb, 16), dtype=torch.int8, device=dev), torch.empty((nb,), **u8),
+                  torch.empty((nb, 1), **u8)) for _ in range(sets)]
+        ys = [torch.empty((rows, cols), dtype=tdt, device=dev) for _ in range(sets)]
+        elem_b = in_b + 1 + 1 / 16 + 1 / 16
+        pk = [lambda x=x, o=o: mxq.mx9_pack(x, out=o) for x, o in zip(xs, packs)]
+        res[f"mx9_pack_{name}"] = dict(workload=f"MX9 pack, {name} weights [4096, 14336]",
+                                       **summarize(time_rotating(pk, launches), rows * cols * elem_b))
+        up = [lambda o=o, y=y: mxq.mx9_unpack(*o, rows, cols, out=y) for o, y in zip(packs, ys)]
+        res[f"mx9_unpack_{name}"] = dict(workload=f"MX9 unpack to {name}, [4096, 14336]",
+                                         **summarize(time_rotating(up, launches), rows * cols * elem_b))
+        del xs, packs, ys, pk, up
+    torch.cuda.synchronize()
+    return res
 
 
 def main():
@@ -85,7 +194,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="multithreaded oracle leg budget")
+    ap.add_argument("--cpu-single-rows", type=int, default=256)
+    ap.add_argument("--skip-configs", action="store_true", help="omit the other workloads")
+    ap.add_argument("--config-launches", type=int, default=30)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -140,11 +252,7 @@ def main():
     elems = M * N
     kbytes = {"dual_axis": elems * DUAL_BYTES_PER_ELEM, "mx9_pack": elems * PACK_BF16_BYTES_PER_ELEM,
               "mx9_unpack": elems * UNPACK_BF16_BYTES_PER_ELEM}
-    kernels = {}
-    for k, ts in per_kernel.items():
-        t = sum(ts) / len(ts)
-        kernels[k] = {"us": round(t * 1e6, 2), "bytes": int(kbytes[k]), "GB_s": round(kbytes[k] / t / 1e9, 1),
-                      "frac": round(kbytes[k] / t / 1e9 / PEAK_HBM_GBS, 4)}
+    kernels = {k: summarize(ts, kbytes[k]) for k, ts in per_kernel.items()}
     step_bytes = sum(kbytes.values())
     ms_per_step = wall / args.steps * 1e3
     value = step_bytes / (wall / args.steps) / 1e9
@@ -189,10 +297,13 @@ def main():
         "copy_GB_s": round(copy_gbs, 1),
         "kernel_source_sha256_16": source_digest(),
     }
+    del x, dual_out, mx9_out, y
+    line["configs"] = None if args.skip_configs else measure_configs(dev, args.config_launches)
     if not args.skip_cpu:
         threads = max(1, min(16, os.cpu_count() or 1))
-        print(f"bench: timing the CPU oracle on {args.cpu_rows} rows, {threads} threads", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(xb, threads, args.cpu_rows)
+        print(f"bench: timing the CPU oracle for {args.cpu_seconds:.0f} s on {threads} threads", file=sys.stderr,
+              flush=True)
+        line["cpu_baseline"] = cpu_baseline(xb, threads, args.cpu_seconds, args.cpu_single_rows)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -112,19 +112,21 @@ def test_repeatable_and_dirty_buffers():
         assert torch.equal(u, v)
 
 
-def test_runs_on_the_callers_stream_and_in_a_graph():
+@pytest.mark.parametrize("N", [384, 1024])   # 1024: rowwise scales staged (two kernels per call)
+def test_runs_on_the_callers_stream_and_in_a_graph(N):
     dev = require_gpu()
-    say("stream and graph capture")
-    xb = synth.special_matrix(256, 384, 8)
-    want = oracle.mxfp8_dual(xb)
+    say(f"stream and graph capture N={N}")
+    M = 256
+    xb = synth.special_matrix(M, N, 8)
+    want = oracle.mxfp8_dual(xb, threads=THREADS)
     xd = bf16_to_dev(xb)
     s = torch.cuda.Stream()
-    out = _dirty_outputs(256, 384, dev)
+    out = _dirty_outputs(M, N, dev)
     with torch.cuda.stream(s):
         mxq.mx_quantize_2d_dual(xd, out=out)
     s.synchronize()
     _assert_equal(out, want, "side stream")
-    out = _dirty_outputs(256, 384, dev)
+    out = _dirty_outputs(M, N, dev)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         mxq.mx_quantize_2d_dual(xd, out=out)
@@ -137,9 +139,10 @@ def test_runs_on_the_callers_stream_and_in_a_graph():
         _assert_equal(out, want, f"graph replay {rep}")
 
 
-def test_grouped_parity_and_tail():
+@pytest.mark.parametrize("N", [256, 1024])   # 1024: rowwise scales staged
+def test_grouped_parity_and_tail(N):
     dev = require_gpu()
-    M, N = 1024, 256
+    M = 1024
     xb = synth.special_matrix(M, N, 9)
     xd = bf16_to_dev(xb)
     cases = [[128, 128, 512], [0, 0, 0], [1024], [256, 256, 768, 768], [0], [384]]

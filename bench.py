@@ -26,7 +26,7 @@ the mixed-magnitude bf16 [8192, 7168] matrix, the grouped cast of bf16
 [16384, 5120] with 64 groups, and MX9 pack/unpack of the fp32 and bf16
 [4096, 14336] weights.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--skip-cpu] [--skip-configs]
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--skip-cpu] [--skip-configs]
 """
 from __future__ import annotations
 
@@ -106,8 +106,11 @@ def time_rotating(calls, launches: int):
     import torch
     for c in calls:
         c()
-    torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for a, b in evs:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
     for i, (a, b) in enumerate(evs):
         a.record()
         calls[i % len(calls)]()
@@ -191,8 +194,8 @@ def measure_configs(dev, launches: int, sets: int = 3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="multithreaded oracle leg budget")
     ap.add_argument("--cpu-single-rows", type=int, default=256)
@@ -235,8 +238,13 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, bracketed by synchronizations
+    # timed region: exactly K steps, bracketed by synchronizations.  torch
+    # creates an event's HIP object at its first record(), so every event is
+    # recorded once here, outside the timed region.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for ev in evs:
+        for e in ev:
+            e.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):

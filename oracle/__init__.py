@@ -249,3 +249,95 @@ def mx9_unpack(q: np.ndarray, max_exp: np.ndarray, prime: np.ndarray, rows: int,
                                            _ptr(y) + r0 * cols * y.itemsize, cols)
     _run([job(a, b) for a, b in _splits(rows, threads)], threads)
     return y
+
+
+def _mx9_code(x: np.ndarray) -> int:
+    if x.dtype in (np.float32, np.uint32):
+        return 0
+    if x.dtype == np.uint16:
+        return 1
+    raise TypeError("fp32 (float32/uint32) or bf16 (uint16 bits) only")
+
+
+def _axis_view(shape, axis: int):
+    shape = tuple(int(s) for s in shape)
+    axis = axis % len(shape)
+    outer = int(np.prod(shape[:axis], dtype=np.int64))
+    inner = int(np.prod(shape[axis + 1:], dtype=np.int64))
+    return outer, shape[axis], inner
+
+
+def mx9_pack_axis(x: np.ndarray, axis: int = -1, threads: int = 1):
+    """Pack a contiguous array in blocks of 16 along `axis` (reading: the axis
+    is moved last before blocking).  Returns (q [nb,16], max_exp [nb],
+    prime [nb,1]) in the order of the moved array's rows."""
+    x = np.ascontiguousarray(x)
+    dtype = _mx9_code(x)
+    outer, length, inner = _axis_view(x.shape, axis)
+    nbl = (length + 15) // 16
+    nb = outer * inner * nbl
+    q = np.empty((nb, 16), np.int8)
+    e = np.empty(nb, np.uint8)
+    p = np.empty((nb, 1), np.uint8)
+    lib = _load()
+    f = lib.oref_mx9_pack_axis
+    f.argtypes = [_P, _I32, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]
+    f.restype = None
+
+    def job(i0, i1):
+        return lambda: f(_ptr(x), dtype, outer, length, inner, i0, i1, _ptr(q), _ptr(e), _ptr(p))
+    _run([job(a, b) for a, b in _splits(inner, threads)], threads)
+    return q, e, p
+
+
+def mx9_unpack_axis(q: np.ndarray, max_exp: np.ndarray, prime: np.ndarray, shape, axis: int = -1,
+                    out_dtype: str = "fp32", threads: int = 1) -> np.ndarray:
+    """Inverse of mx9_pack_axis: an array of `shape`, float32 for "fp32" or
+    uint16 bf16 bits for "bf16"."""
+    outer, length, inner = _axis_view(shape, axis)
+    nb = outer * inner * ((length + 15) // 16)
+    q = np.ascontiguousarray(q, dtype=np.int8).reshape(nb, 16)
+    max_exp = np.ascontiguousarray(max_exp, dtype=np.uint8).reshape(nb)
+    prime = np.ascontiguousarray(prime, dtype=np.uint8).reshape(nb)
+    od, ty = {"fp32": (0, np.float32), "bf16": (1, np.uint16)}[out_dtype]
+    y = np.empty(tuple(shape), ty)
+    lib = _load()
+    f = lib.oref_mx9_unpack_axis
+    f.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I32, _P]
+    f.restype = None
+
+    def job(i0, i1):
+        return lambda: f(_ptr(q), _ptr(max_exp), _ptr(prime), outer, length, inner, i0, i1, od, _ptr(y))
+    _run([job(a, b) for a, b in _splits(inner, threads)], threads)
+    return y
+
+
+def mx9_to_records(q: np.ndarray, max_exp: np.ndarray, prime: np.ndarray, rows: int, bpr: int) -> np.ndarray:
+    """The single-byte-tensor form: uint8 [rows, 18 * bpr], one 18-byte record
+    per block (exponent byte, q[16], prime)."""
+    nb = rows * bpr
+    q = np.ascontiguousarray(q, dtype=np.int8).reshape(nb, 16)
+    max_exp = np.ascontiguousarray(max_exp, dtype=np.uint8).reshape(nb)
+    prime = np.ascontiguousarray(prime, dtype=np.uint8).reshape(nb)
+    out = np.empty((rows, 18 * bpr), np.uint8)
+    f = _load().oref_mx9_to_records
+    f.argtypes = [_P, _P, _P, _I64, _I64, _P, _I64]
+    f.restype = None
+    f(_ptr(q), _ptr(max_exp), _ptr(prime), rows, bpr, _ptr(out), 18 * bpr)
+    return out
+
+
+def mx9_from_records(packed: np.ndarray, rows: int, bpr: int):
+    """Split [rows, >= 18 * bpr] records back into (q, max_exp, prime)."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    if packed.ndim != 2 or packed.strides[1] != 1 or packed.shape[0] != rows or packed.shape[1] < 18 * bpr:
+        raise ValueError("expected uint8 [rows, >= 18 * bpr] with contiguous rows")
+    nb = rows * bpr
+    q = np.empty((nb, 16), np.int8)
+    e = np.empty(nb, np.uint8)
+    p = np.empty((nb, 1), np.uint8)
+    f = _load().oref_mx9_from_records
+    f.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P]
+    f.restype = None
+    f(_ptr(packed), packed.strides[0], rows, bpr, _ptr(q), _ptr(e), _ptr(p))
+    return q, e, p

@@ -30,10 +30,15 @@
  *     2^E, the block's shared power of two; bit j belongs to pair j, LSB first.
  *   - MX9 non-finite block: max_exp 255, q all 0, prime 0, unpacks to NaN.
  *   - MX9 trailing partial block is padded with +0.
+ *   - MX9 along another axis: the axis is moved last (movedim) before
+ *     blocking, which fixes the block order.
+ *   - MX9 in one byte tensor: 18-byte records, exponent byte, q[16], prime.
  *
  * Parity unpinned (oracle-defined; no passage and no independent source fixes
  * them): the 0x7F byte of poisoned MXFP8 blocks, the row-major s_col layout,
- * the MX9 pair-bit polarity and bit order, and the MX9 poison values.  Every
+ * the MX9 pair-bit polarity and bit order, the MX9 poison values, the block
+ * order for a non-last axis and the place of q and prime inside an MX9
+ * record.  Every
  * other result is pinned by the test suite against the pages' constants,
  * hand-derived blocks, torch's float8 codec, closed forms or exact rationals.
  */
@@ -387,6 +392,101 @@ void oref_mx9_unpack(const int8_t *q, const uint8_t *max_exp, const uint8_t *pri
                            : bf16_round(ldexp((double)q[16 * blk + i], S - 127 - 6 - p));
                 ((uint16_t *)y)[r * ld_y + c] = h;
             }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* MX9 along any axis   [MX9] (the axis argument of the MX9 calls)          */
+/* ------------------------------------------------------------------------ */
+
+/* The array is contiguous and viewed as x[outer][len][inner]; blocks of 16
+ * run along len.  Reading: the axis is first moved to the last position
+ * (movedim(axis, -1)), so row (o, i) of the moved array is x[o][0..len-1][i]
+ * and the block order is (o, i, j), j = block within the row,
+ * ceil(len/16) blocks per row.  Each row is packed exactly as
+ * oref_mx9_pack packs one row.  This call handles the rows with
+ * i0 <= i < i1, for every o. */
+void oref_mx9_pack_axis(const void *x, int dtype, int64_t outer, int64_t len, int64_t inner,
+                        int64_t i0, int64_t i1, int8_t *q, uint8_t *max_exp, uint8_t *prime)
+{
+    int64_t nbl = (len + 15) / 16, o, i, l;
+    size_t es = dtype == 0 ? 4 : 2;
+    unsigned char row[4 * 16 * 1024];      /* one moved row, in chunks of 16 Ki elements */
+    for (o = 0; o < outer; o++) {
+        for (i = i0; i < i1; i++) {
+            int64_t blk0 = (o * inner + i) * nbl, done;
+            for (done = 0; done < len; done += 16 * 1024) {
+                int64_t n = len - done < 16 * 1024 ? len - done : 16 * 1024;
+                for (l = 0; l < n; l++)
+                    memcpy(row + l * es, (const unsigned char *)x + (size_t)((o * len + done + l) * inner + i) * es, es);
+                oref_mx9_pack(row, dtype, 1, n, n, q + 16 * (blk0 + done / 16),
+                              max_exp + blk0 + done / 16, prime + blk0 + done / 16);
+            }
+        }
+    }
+}
+
+/* Inverse of oref_mx9_pack_axis: unpack row (o, i) as oref_mx9_unpack unpacks
+ * one row and place element l at y[o][l][i]. */
+void oref_mx9_unpack_axis(const int8_t *q, const uint8_t *max_exp, const uint8_t *prime,
+                          int64_t outer, int64_t len, int64_t inner, int64_t i0, int64_t i1,
+                          int out_dtype, void *y)
+{
+    int64_t nbl = (len + 15) / 16, o, i, l;
+    size_t es = out_dtype == 0 ? 4 : 2;
+    unsigned char row[4 * 16 * 1024];
+    for (o = 0; o < outer; o++) {
+        for (i = i0; i < i1; i++) {
+            int64_t blk0 = (o * inner + i) * nbl, done;
+            for (done = 0; done < len; done += 16 * 1024) {
+                int64_t n = len - done < 16 * 1024 ? len - done : 16 * 1024;
+                oref_mx9_unpack(q + 16 * (blk0 + done / 16), max_exp + blk0 + done / 16,
+                                prime + blk0 + done / 16, 1, n, out_dtype, row, n);
+                for (l = 0; l < n; l++)
+                    memcpy((unsigned char *)y + (size_t)((o * len + done + l) * inner + i) * es, row + l * es, es);
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* MX9 in one byte tensor   [MX9] (commit "pack mx9 into a single uint8     */
+/* tensor"; the exponent byte is stored at blk * N_PACKED_BYTES)            */
+/* ------------------------------------------------------------------------ */
+
+/* One 18-byte record per block: the E8M0 exponent byte first (the pages
+ * place it at the record's start), then q[0..15], then the prime byte
+ * (reading: the order of q and prime inside the record is not printed).
+ * Rows of bpr records sit at a pitch of ld_p bytes; bytes past 18 * bpr in a
+ * row are not touched. */
+void oref_mx9_to_records(const int8_t *q, const uint8_t *max_exp, const uint8_t *prime,
+                         int64_t rows, int64_t bpr, uint8_t *packed, int64_t ld_p)
+{
+    int64_t r, b;
+    for (r = 0; r < rows; r++) {
+        for (b = 0; b < bpr; b++) {
+            int64_t blk = r * bpr + b;
+            uint8_t *rec = packed + r * ld_p + 18 * b;
+            rec[0] = max_exp[blk];
+            memcpy(rec + 1, q + 16 * blk, 16);
+            rec[17] = prime[blk];
+        }
+    }
+}
+
+/* Inverse of oref_mx9_to_records. */
+void oref_mx9_from_records(const uint8_t *packed, int64_t ld_p, int64_t rows, int64_t bpr,
+                           int8_t *q, uint8_t *max_exp, uint8_t *prime)
+{
+    int64_t r, b;
+    for (r = 0; r < rows; r++) {
+        for (b = 0; b < bpr; b++) {
+            int64_t blk = r * bpr + b;
+            const uint8_t *rec = packed + r * ld_p + 18 * b;
+            max_exp[blk] = rec[0];
+            memcpy(q + 16 * blk, rec + 1, 16);
+            prime[blk] = rec[17];
         }
     }
 }

@@ -24,7 +24,8 @@ while rotating three input/output buffer sets so that MI355X's 256 MB
 last-level cache cannot serve a call from the previous one: the dense cast of
 the mixed-magnitude bf16 [8192, 7168] matrix, the grouped cast of bf16
 [16384, 5120] with 64 groups, and MX9 pack/unpack of the fp32 and bf16
-[4096, 14336] weights.  It also holds the dual-axis cast of the stress matrix
+[4096, 14336] weights in three forms: three tensors along the last axis,
+one tensor of 18-byte records, and three tensors along axis 0.  It also holds the dual-axis cast of the stress matrix
 timed alone (back-to-back calls): inside the step the cast starts while the
 previous step's MX9 unpack writes are still draining to HBM, so its in-step
 time is longer than its time alone.
@@ -236,6 +237,25 @@ def measure_configs(dev, launches: int, sets: int = 3):
         up = [lambda o=o, y=y: mxq.mx9_unpack(*o, rows, cols, out=y) for o, y in zip(packs, ys)]
         res[f"mx9_unpack_{name}"] = dict(workload=f"MX9 unpack to {name}, [4096, 14336]",
                                          **summarize(time_rotating(up, launches), rows * cols * elem_b))
+        del packs, pk, up
+        # the same weights as one byte tensor of 18-byte records (last axis)
+        recs = [torch.empty((rows, cols // 16 * 18), **u8) for _ in range(sets)]
+        pk = [lambda x=x, o=o: mxq.mx9_pack_records(x, -1, out=o) for x, o in zip(xs, recs)]
+        res[f"mx9_pack_records_{name}"] = dict(workload=f"MX9 pack to 18-byte records, {name} weights [4096, 14336]",
+                                               **summarize(time_rotating(pk, launches), rows * cols * elem_b))
+        up = [lambda o=o, y=y: mxq.mx9_unpack_records(o, (rows, cols), -1, out=y) for o, y in zip(recs, ys)]
+        res[f"mx9_unpack_records_{name}"] = dict(workload=f"MX9 unpack from records to {name}, [4096, 14336]",
+                                                 **summarize(time_rotating(up, launches), rows * cols * elem_b))
+        del recs, pk, up
+        # blocks along axis 0 (down the columns) of the same weights
+        packs = [(torch.empty((nb, 16), dtype=torch.int8, device=dev), torch.empty((nb,), **u8),
+                  torch.empty((nb, 1), **u8)) for _ in range(sets)]
+        pk = [lambda x=x, o=o: mxq.mx9_pack_axis(x, 0, out=o) for x, o in zip(xs, packs)]
+        res[f"mx9_pack_axis0_{name}"] = dict(workload=f"MX9 pack along axis 0, {name} weights [4096, 14336]",
+                                             **summarize(time_rotating(pk, launches), rows * cols * elem_b))
+        up = [lambda o=o, y=y: mxq.mx9_unpack_axis(*o, (rows, cols), 0, out=y) for o, y in zip(packs, ys)]
+        res[f"mx9_unpack_axis0_{name}"] = dict(workload=f"MX9 unpack along axis 0 to {name}, [4096, 14336]",
+                                               **summarize(time_rotating(up, launches), rows * cols * elem_b))
         del xs, packs, ys, pk, up
     torch.cuda.synchronize()
     return res

@@ -160,6 +160,71 @@ int mx9_unpack(const int8_t *q, const uint8_t *max_exp, const uint8_t *prime,
                int64_t rows, int64_t cols, int32_t block_size, int32_t out_dtype,
                void *y, int64_t ld_y, void *stream);
 
+/*
+ * mx9_pack_axis -- MX9 pack in blocks of 16 along any axis ([MX9], the
+ * calls' axis argument; the shape and the axis are not stored, so the caller
+ * passes them back to the unpack).
+ *
+ *   x        contiguous fp32 or bf16 array viewed as [outer, len, inner]: the
+ *            blocked axis has len elements, outer is the product of the
+ *            dimensions before it and inner of those after it (inner == 1 is
+ *            the last axis, identical to mx9_pack with rows = outer).
+ *   Reading (the page does not print the block order): the axis is moved
+ *   last before blocking, so block (o, i, j) holds x[o][16j .. 16j+15][i],
+ *   padded with +0 past len, and is numbered (o * inner + i) * nbl + j,
+ *   nbl = ceil(len / 16).
+ *   q, max_exp, prime  as for mx9_pack, nb = outer * inner * nbl blocks.
+ *
+ * Errors: MX_E_NULL, MX_E_DTYPE, MX_E_BLOCK (block_size != 16), MX_E_SHAPE
+ * (a negative or too large dimension), MX_E_ALIGN (x not aligned to its
+ * element size, q not 16-byte aligned), MX_E_OVERLAP.  A zero dimension is
+ * a no-op.
+ */
+int mx9_pack_axis(const void *x, int32_t dtype, int64_t outer, int64_t len, int64_t inner,
+                  int32_t block_size, int8_t *q, uint8_t *max_exp, uint8_t *prime, void *stream);
+
+/*
+ * mx9_unpack_axis -- inverse of mx9_pack_axis: y (contiguous [outer, len,
+ * inner], fp32 or bf16 by out_dtype) gets every element, computed as in
+ * mx9_unpack.  Errors as for mx9_unpack, with the shape checks of
+ * mx9_pack_axis.
+ */
+int mx9_unpack_axis(const int8_t *q, const uint8_t *max_exp, const uint8_t *prime, int64_t outer,
+                    int64_t len, int64_t inner, int32_t block_size, int32_t out_dtype, void *y,
+                    void *stream);
+
+/*
+ * mx9_pack_records -- MX9 in one byte tensor ([MX9], commit "refactor: mx:
+ * pack mx9 into a single uint8 tensor", which stores the exponent byte at
+ * the start of each block's record).
+ *
+ *   x       as for mx9_pack_axis (blocks along the middle axis of [outer,
+ *           len, inner]; inner == 1 is the last axis).
+ *   packed  uint8, outer * inner rows of nbl records at a pitch of ld_p
+ *           bytes (ld_p >= 18 * nbl); row o * inner + i holds the blocks
+ *           (o, i, 0 .. nbl-1).  A record is 18 bytes: the exponent byte,
+ *           q[0..15], the prime byte (reading: the page fixes only the
+ *           exponent byte's place).  Bytes past 18 * nbl in a row are not
+ *           written.  9 bits per element.
+ *
+ * Errors: MX_E_NULL, MX_E_DTYPE, MX_E_BLOCK, MX_E_SHAPE, MX_E_STRIDE
+ * (ld_p < 18 * nbl or above 2^40), MX_E_ALIGN (x not aligned to its element
+ * size), MX_E_OVERLAP.  A zero dimension is a no-op.  Contiguous records of
+ * a last-axis pack whose len is a multiple of 16, with x and packed 16-byte
+ * aligned, take the fastest path.
+ */
+int mx9_pack_records(const void *x, int32_t dtype, int64_t outer, int64_t len, int64_t inner,
+                     int32_t block_size, uint8_t *packed, int64_t ld_p, void *stream);
+
+/*
+ * mx9_unpack_records -- inverse of mx9_pack_records into a contiguous
+ * [outer, len, inner] y of out_dtype (fp32 or bf16), computed as in
+ * mx9_unpack.  Errors: MX_E_NULL, MX_E_DTYPE, MX_E_BLOCK, MX_E_SHAPE,
+ * MX_E_STRIDE, MX_E_ALIGN (y not aligned to its element size), MX_E_OVERLAP.
+ */
+int mx9_unpack_records(const uint8_t *packed, int64_t ld_p, int64_t outer, int64_t len, int64_t inner,
+                       int32_t block_size, int32_t out_dtype, void *y, void *stream);
+
 /* Host function: a static, human-readable name for an mx_status value. */
 const char *mx_status_string(int status);
 

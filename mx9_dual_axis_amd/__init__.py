@@ -11,9 +11,12 @@ Entry points (same names as the C ABI):
   mx_quantize_grouped(x, offs, err=None) -> (q_row, s_row, q_col, s_col)
   mx9_pack(x)                            -> (q, max_exp, prime)
   mx9_unpack(q, max_exp, prime, rows, cols, out_dtype) -> y
+  mx9_pack_axis(x, axis) / mx9_unpack_axis(q, max_exp, prime, shape, axis)
+  mx9_pack_records(x, axis) -> packed uint8 / mx9_unpack_records(packed, shape, axis)
 plus the signatures the pages use: ``mxfp8_quantize_2d_1x32_32x1`` (dense
 when ``offs`` is None, grouped otherwise), ``convert_to_mx9`` and
-``convert_from_mx9``.
+``convert_from_mx9`` (with an axis), and their single-tensor forms
+``convert_to_mx9_packed`` / ``convert_from_mx9_packed``.
 """
 from __future__ import annotations
 
@@ -54,7 +57,12 @@ def _load():
     lib.mx_quantize_grouped.argtypes = [P, I64, I64, I64, I32, I32, P, I32, P, P, P, P, P, P]
     lib.mx9_pack.argtypes = [P, I32, I64, I64, I64, I32, P, P, P, P]
     lib.mx9_unpack.argtypes = [P, P, P, I64, I64, I32, I32, P, I64, P]
-    for f in (lib.mx_quantize_2d_dual, lib.mx_quantize_grouped, lib.mx9_pack, lib.mx9_unpack):
+    lib.mx9_pack_axis.argtypes = [P, I32, I64, I64, I64, I32, P, P, P, P]
+    lib.mx9_unpack_axis.argtypes = [P, P, P, I64, I64, I64, I32, I32, P, P]
+    lib.mx9_pack_records.argtypes = [P, I32, I64, I64, I64, I32, P, I64, P]
+    lib.mx9_unpack_records.argtypes = [P, I64, I64, I64, I64, I32, I32, P, P]
+    for f in (lib.mx_quantize_2d_dual, lib.mx_quantize_grouped, lib.mx9_pack, lib.mx9_unpack,
+              lib.mx9_pack_axis, lib.mx9_unpack_axis, lib.mx9_pack_records, lib.mx9_unpack_records):
         f.restype = ctypes.c_int
     lib.mx_status_string.argtypes = [ctypes.c_int]
     lib.mx_status_string.restype = ctypes.c_char_p
@@ -202,6 +210,111 @@ def mx9_unpack(q: torch.Tensor, max_exp: torch.Tensor, prime: torch.Tensor, rows
     return y
 
 
+def _axis_dims(shape, axis: int):
+    """(outer, len, inner) of a contiguous array of `shape` blocked along `axis`."""
+    shape = tuple(int(d) for d in shape)
+    if not shape:
+        raise ValueError("a 0-d tensor has no axis to block")
+    axis = axis % len(shape)
+    outer = 1
+    for d in shape[:axis]:
+        outer *= d
+    inner = 1
+    for d in shape[axis + 1:]:
+        inner *= d
+    return outer, shape[axis], inner
+
+
+def _out_code(out_dtype) -> int:
+    return {torch.float32: MX_DTYPE_F32, torch.bfloat16: MX_DTYPE_BF16}.get(out_dtype, 2)
+
+
+def mx9_pack_axis(x: torch.Tensor, axis: int = -1, block_size: int = 16, out=None):
+    """MX9 pack of a contiguous fp32/bf16 tensor in blocks of 16 along `axis`
+    (the axis moved last before blocking).  Returns q int8 [nb,16], max_exp
+    uint8 [nb], prime uint8 [nb,1] with blocks ordered (outer, inner, block)."""
+    _need_cuda(x, "x")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    outer, length, inner = _axis_dims(x.shape, axis)
+    nb = outer * inner * ((length + 15) // 16)
+    if out is None:
+        q = torch.empty((nb, 16), dtype=torch.int8, device=x.device)
+        e = torch.empty((nb,), dtype=torch.uint8, device=x.device)
+        p = torch.empty((nb, 1), dtype=torch.uint8, device=x.device)
+    else:
+        q, e, p = out
+    _check(_load().mx9_pack_axis(x.data_ptr(), _mx9_dtype(x), outer, length, inner, block_size,
+                                 q.data_ptr(), e.data_ptr(), p.data_ptr(), _stream(x.device)))
+    return q, e, p
+
+
+def mx9_unpack_axis(q: torch.Tensor, max_exp: torch.Tensor, prime: torch.Tensor, shape, axis: int = -1,
+                    out_dtype=torch.float32, block_size: int = 16, out: torch.Tensor | None = None):
+    """Inverse of mx9_pack_axis: a contiguous tensor of `shape` and out_dtype."""
+    for t, n in ((q, "q"), (max_exp, "max_exp"), (prime, "prime")):
+        _need_cuda(t, n)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    outer, length, inner = _axis_dims(shape, axis)
+    nb = outer * inner * ((length + 15) // 16)
+    if q.numel() != nb * 16 or max_exp.numel() != nb or prime.numel() != nb:
+        raise ValueError("q / max_exp / prime sizes do not match the shape")
+    if out is None:
+        od = _out_code(out_dtype)
+        y = torch.empty(tuple(shape), dtype=out_dtype if od != 2 else torch.float32, device=q.device)
+    else:
+        y = out
+        od = _out_code(y.dtype)
+        if not y.is_contiguous() or tuple(y.shape) != tuple(shape):
+            raise ValueError("out must be contiguous with the given shape")
+    _check(_load().mx9_unpack_axis(q.data_ptr(), max_exp.data_ptr(), prime.data_ptr(), outer, length, inner,
+                                   block_size, od, y.data_ptr(), _stream(q.device)))
+    return y
+
+
+def mx9_pack_records(x: torch.Tensor, axis: int = -1, block_size: int = 16, out: torch.Tensor | None = None):
+    """MX9 in one byte tensor: uint8 [outer*inner, 18*nbl], one 18-byte record
+    per block (exponent byte, q[16], prime byte).  `out` may be a wider uint8
+    [outer*inner, >= 18*nbl] tensor with contiguous rows (its row pitch is
+    passed to the library)."""
+    _need_cuda(x, "x")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    outer, length, inner = _axis_dims(x.shape, axis)
+    row = 18 * ((length + 15) // 16)
+    if out is None:
+        out = torch.empty((outer * inner, row), dtype=torch.uint8, device=x.device)
+    elif (out.dtype != torch.uint8 or out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != outer * inner
+          or out.shape[1] < row):
+        raise ValueError("out must be uint8 [outer*inner, >= 18*nbl] with contiguous rows")
+    _check(_load().mx9_pack_records(x.data_ptr(), _mx9_dtype(x), outer, length, inner, block_size,
+                                    out.data_ptr(), out.stride(0), _stream(x.device)))
+    return out
+
+
+def mx9_unpack_records(packed: torch.Tensor, shape, axis: int = -1, out_dtype=torch.float32,
+                       block_size: int = 16, out: torch.Tensor | None = None):
+    """Inverse of mx9_pack_records: a contiguous tensor of `shape`."""
+    _need_cuda(packed, "packed")
+    outer, length, inner = _axis_dims(shape, axis)
+    row = 18 * ((length + 15) // 16)
+    if (packed.dtype != torch.uint8 or packed.dim() != 2 or packed.stride(1) != 1
+            or packed.shape[0] != outer * inner or packed.shape[1] < row):
+        raise ValueError("packed must be uint8 [outer*inner, >= 18*nbl] with contiguous rows")
+    if out is None:
+        od = _out_code(out_dtype)
+        y = torch.empty(tuple(shape), dtype=out_dtype if od != 2 else torch.float32, device=packed.device)
+    else:
+        y = out
+        od = _out_code(y.dtype)
+        if not y.is_contiguous() or tuple(y.shape) != tuple(shape):
+            raise ValueError("out must be contiguous with the given shape")
+    _check(_load().mx9_unpack_records(packed.data_ptr(), packed.stride(0), outer, length, inner, block_size, od,
+                                      y.data_ptr(), _stream(packed.device)))
+    return y
+
+
 # --- the pages' call signatures ------------------------------------------
 
 def mxfp8_quantize_2d_1x32_32x1(x: torch.Tensor, block_size: int = 32, scaling_mode="rceil",
@@ -212,14 +325,30 @@ def mxfp8_quantize_2d_1x32_32x1(x: torch.Tensor, block_size: int = 32, scaling_m
     return mx_quantize_grouped(x, offs, block_size, scaling_mode)
 
 
-def convert_to_mx9(x: torch.Tensor, block_size: int = 16):
-    return mx9_pack(x.reshape(-1, x.shape[-1]), block_size)
+def convert_to_mx9(x: torch.Tensor, block_size: int = 16, axis: int = -1):
+    """Three-part MX9 (q, max_exp, prime) in blocks along `axis`."""
+    if axis % x.dim() == x.dim() - 1:
+        return mx9_pack(x.reshape(-1, x.shape[-1]), block_size)
+    return mx9_pack_axis(x, axis, block_size)
 
 
-def convert_from_mx9(q, max_exp, prime, out_dtype, shape, block_size: int = 16):
+def convert_from_mx9(q, max_exp, prime, out_dtype, shape, block_size: int = 16, axis: int = -1):
+    """Inverse of convert_to_mx9; the shape and axis are not stored."""
     shape = tuple(shape)
-    cols = shape[-1]
-    rows = 1
-    for s in shape[:-1]:
-        rows *= s
-    return mx9_unpack(q, max_exp, prime, rows, cols, out_dtype, block_size).reshape(shape)
+    if axis % len(shape) == len(shape) - 1:
+        cols = shape[-1]
+        rows = 1
+        for s in shape[:-1]:
+            rows *= s
+        return mx9_unpack(q, max_exp, prime, rows, cols, out_dtype, block_size).reshape(shape)
+    return mx9_unpack_axis(q, max_exp, prime, shape, axis, out_dtype, block_size)
+
+
+def convert_to_mx9_packed(x: torch.Tensor, block_size: int = 16, axis: int = -1):
+    """MX9 in one uint8 tensor of 18-byte records (exponent byte first)."""
+    return mx9_pack_records(x, axis, block_size)
+
+
+def convert_from_mx9_packed(packed, out_dtype, shape, block_size: int = 16, axis: int = -1):
+    """Inverse of convert_to_mx9_packed; the shape and axis are not stored."""
+    return mx9_unpack_records(packed, shape, axis, out_dtype, block_size)

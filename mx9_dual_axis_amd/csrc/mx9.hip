@@ -18,81 +18,16 @@
 // rounded half-to-even by v_rndne_f32; fp32 denormals are kept (no flush),
 // so subnormal inputs quantize exactly.
 #include "mxq_kernels.h"
+#include "mx9_codec.h"
 
 namespace mxq {
 namespace {
 
+using namespace mx9;
+
 constexpr int kThreads = 256;
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-
-// round-half-even(x * 2^shift) clamped to [-127, 127], returned in the low
-// byte of the result (two's complement).  |x * 2^shift| < 2^8 for every
-// element of a block, and ldexp is exact there.  Clamping to +-127 before
-// rounding equals clamping after (the bounds are integers).  Adding 1.5*2^23
-// rounds half-to-even to an integer held in the low mantissa bits, whose low
-// byte is the two's-complement int8 of the rounded value.
-__device__ __forceinline__ uint32_t qbits(uint32_t w, int shift) {
-    float t = __builtin_ldexpf(__uint_as_float(w), shift);
-    t = __builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
-    return __float_as_uint(t + 12582912.0f);
-}
-
-// Low bytes of four qbits results -> one dword, element a in byte 0.
-__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
-    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
-    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
-}
-
-// Quantize pairs of fp32 patterns against the block's shared exponent byte S.
-// A pair is demoted (p = 1) when its larger magnitude is below 2^(S-127),
-// i.e. when its larger magnitude pattern is below S << 23 (magnitudes and
-// their bit patterns order alike).  Returns the q bytes of kPairs pairs in
-// kPairs / 2 dwords and the pair bits in *bits (LSB = first pair).
-template <int kPairs>
-__device__ __forceinline__ void quantize_pairs(const uint32_t (&w)[2 * kPairs], uint32_t S,
-                                               uint32_t (&qd)[kPairs / 2], uint32_t& bits) {
-    uint32_t qb[2 * kPairs];
-    bits = 0;
-#pragma unroll
-    for (int j = 0; j < kPairs; ++j) {
-        const uint32_t pm = max(w[2 * j] & 0x7FFFFFFFu, w[2 * j + 1] & 0x7FFFFFFFu);
-        const uint32_t p = pm < (S << 23) ? 1u : 0u;
-        bits |= p << j;
-        const int shift = 133 + int(p) - int(S);          // 6 + p - E, E = S - 127
-        qb[2 * j] = qbits(w[2 * j], shift);
-        qb[2 * j + 1] = qbits(w[2 * j + 1], shift);
-    }
-#pragma unroll
-    for (int k = 0; k < kPairs / 2; ++k) qd[k] = pack4(qb[4 * k], qb[4 * k + 1], qb[4 * k + 2], qb[4 * k + 3]);
-}
-
-// Largest magnitude pattern of n fp32 patterns (NaN > Inf > finite).
-template <int kN>
-__device__ __forceinline__ uint32_t max_magnitude(const uint32_t (&w)[kN]) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < kN; ++i) m = max(m, w[i] & 0x7FFFFFFFu);
-    return m;
-}
-
-// Pack 16 fp32 patterns: q bytes (4 dwords), max_exp byte, prime byte.
-// The shared exponent byte is the largest exponent field raised to >= 1;
-// an Inf or NaN (exponent field 255) poisons the block.
-__device__ __forceinline__ void pack16(const uint32_t (&w)[16], uint32_t (&qd)[4], uint32_t& me,
-                                       uint32_t& pr) {
-    const uint32_t mmax = max_magnitude(w);
-    const uint32_t S = max(mmax >> 23, 1u);
-    quantize_pairs<8>(w, S, qd, pr);
-    me = S;
-    if (mmax >= 0x7F800000u) {          // Inf or NaN: poisoned block
-        qd[0] = qd[1] = qd[2] = qd[3] = 0u;
-        me = 255u;
-        pr = 0u;
-    }
-}
 
 // Vector path: cols % 16 == 0 and 16-byte aligned block starts.
 template <int kDtype>
@@ -159,26 +94,6 @@ void mx9_pack_any(const void* __restrict__ xv, int64_t ld_x, int64_t cols, uint3
     prime[blk] = uint8_t(pr);
 }
 
-// Unpack one block to 16 fp32 values: q * 2^(S - 133 - p); S == 255 -> NaN.
-__device__ __forceinline__ void unpack16(uint4 qv, uint32_t S, uint32_t pr, float (&y)[16]) {
-    const uint32_t qd[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int qi = int(int8_t(uint8_t(qd[i >> 2] >> (8 * (i & 3)))));
-        const int p = int((pr >> (i >> 1)) & 1u);
-        y[i] = __builtin_ldexpf(float(qi), int(S) - 133 - p);
-    }
-    if (S == 255u) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) y[i] = __uint_as_float(0x7FC00000u);
-    }
-}
-
-__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
-    const bf16x2 r = {__bf16(lo), __bf16(hi)};
-    return __builtin_bit_cast(uint32_t, r);
-}
-
 // ---------------------------------------------------------------------------
 // Flat paths: the input is one contiguous run of nb blocks (ld == cols and
 // cols % 16 == 0).  A block is shared by L = 16 * esz / 16 lanes (2 for bf16,
@@ -187,48 +102,22 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
 // prime bits are combined across the L lanes with DPP quad permutes.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
-    return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0xB1, 0xF, 0xF, true));
-}
-__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {
-    return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x4E, 0xF, 0xF, true));
-}
-
 // One pass of the flat pack: this lane's 16-byte piece of block blk.
 template <int kDtype, bool kGuard>
 __device__ __forceinline__ void pack_piece(const void* __restrict__ xv, uint64_t nb, uint64_t blk,
                                            uint32_t part, int8_t* __restrict__ q,
                                            uint8_t* __restrict__ max_exp, uint8_t* __restrict__ prime) {
-    constexpr int kLanes = kDtype == 0 ? 4 : 2;          // lanes per block
-    constexpr int kElems = 16 / kLanes;                   // elements per lane
+    using P = FlatPiece<kDtype>;
     const bool live = !kGuard || blk < nb;
-    uint32_t w[kElems];
     uint4 d = make_uint4(0u, 0u, 0u, 0u);
-    if (live) d = reinterpret_cast<const uint4*>(xv)[blk * kLanes + part];
-    if (kDtype == 0) {
-        w[0] = d.x; w[1] = d.y; w[2] = d.z; w[3] = d.w;
-    } else {
-        const uint32_t dd[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { w[2 * i] = dd[i] << 16; w[2 * i + 1] = dd[i] & 0xFFFF0000u; }
-    }
-    uint32_t mmax = max_magnitude(w);
-    mmax = max(mmax, dpp_xor1(mmax));
-    if (kLanes == 4) mmax = max(mmax, dpp_xor2(mmax));
-    const uint32_t S = max(mmax >> 23, 1u);
-    uint32_t qd[kElems / 4], bits;
-    quantize_pairs<kElems / 2>(w, S, qd, bits);
-    // the block's prime byte: this lane's pairs start at bit (kElems / 2) * part
-    uint32_t pr = bits << ((kElems / 2) * part);
-    pr |= dpp_xor1(pr);
-    if (kLanes == 4) pr |= dpp_xor2(pr);
-    const bool poison = mmax >= 0x7F800000u;
+    if (live) d = reinterpret_cast<const uint4*>(xv)[blk * P::kLanes + part];
+    const P r = pack_flat_piece<kDtype>(d, part);
     if (live) {
-        uint8_t* qb = reinterpret_cast<uint8_t*>(q) + blk * 16 + part * kElems;
-        if (kElems == 8) *reinterpret_cast<uint2*>(qb) = poison ? make_uint2(0u, 0u) : make_uint2(qd[0], qd[1]);
-        else *reinterpret_cast<uint32_t*>(qb) = poison ? 0u : qd[0];
-        if (part == 0) max_exp[blk] = uint8_t(poison ? 255u : S);
-        if (part == 1) prime[blk] = uint8_t(poison ? 0u : pr);
+        uint8_t* qb = reinterpret_cast<uint8_t*>(q) + blk * 16 + part * P::kElems;
+        if (P::kElems == 8) *reinterpret_cast<uint2*>(qb) = make_uint2(r.qd[0], r.qd[1]);
+        else *reinterpret_cast<uint32_t*>(qb) = r.qd[0];
+        if (part == 0) max_exp[blk] = uint8_t(r.S);
+        if (part == 1) prime[blk] = uint8_t(r.prime);
     }
 }
 

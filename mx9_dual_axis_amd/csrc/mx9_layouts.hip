@@ -1,0 +1,634 @@
+// mx9_layouts.hip -- MX9 along any axis and in the single-byte-tensor form,
+// for gfx950 (CDNA4).
+//
+// Format and calls: AMD-AGI/ALTO PR #33, "feat: mx9: add fused MX9
+// quantization kernel with pack/unpack": the calls take an axis argument and
+// do not store the shape or the axis (the caller passes them back), and the
+// commit "refactor: mx: pack mx9 into a single uint8 tensor" stores each
+// block as one record that starts with its exponent byte (the kernel writes
+// it at blk * N_PACKED_BYTES).  Readings taken here: the axis is moved last
+// before blocking, so block (o, i, j) of a contiguous [outer, len, inner]
+// array covers x[o][16j .. 16j+15][i] and is numbered (o * inner + i) * nbl
+// + j with nbl = ceil(len / 16); a record is 18 bytes: the exponent byte,
+// q[0..15], then the prime byte; records of one (o, i) form a row, and rows
+// sit at a caller-given pitch.
+//
+// Kernels:
+//   * flat records: contiguous input blocks and contiguous records.  The
+//     lanes hold blocks exactly as the flat three-part pack does (a block
+//     over 2 lanes for bf16, 4 for fp32; every wave-wide load is one
+//     contiguous range); the workgroup's records are assembled in LDS and
+//     written as 16-byte chunks, so the 18-byte records cost no unaligned
+//     global stores.  The unpack stages the records the same way.
+//   * axis tiles (inner > 1): a workgroup takes 64 consecutive inner
+//     positions i of one o and 32 consecutive blocks j (128 and 16 when the
+//     inner extent is even: a lane then takes two adjacent i, so one 32-bit
+//     load carries two bf16 elements and one 64-bit load two fp32).  The 64
+//     lanes of a wave take consecutive i, so every load instruction reads a
+//     contiguous run of the inner axis.  The tile's outputs are staged in
+//     LDS (rows padded so the column-wise writes do not collide in the banks)
+//     and written row by row: each (o, i) receives 512 contiguous q bytes
+//     (576 record bytes) and 32 max_exp and prime bytes (256, 288 and 16 with
+//     two positions per lane), so q lines are never assembled from pieces of
+//     different workgroups.  The unpack reads a tile's rows the same way and
+//     writes each element row of the tile as one contiguous run of the inner
+//     axis.
+//   * strided (inner == 1): records with a pitch or a ragged row, one thread
+//     per block.
+#include "mxq_kernels.h"
+#include "mx9_codec.h"
+
+namespace mxq {
+namespace {
+
+using namespace mx9;
+
+constexpr int kThreads = 256;
+constexpr int kRec = 18;          // bytes per block record: exponent, q[16], prime
+
+__device__ __forceinline__ uint32_t load_bits(const void* xv, uint64_t idx, int dtype) {
+    return dtype == 0 ? static_cast<const uint32_t*>(xv)[idx]
+                      : uint32_t(static_cast<const uint16_t*>(xv)[idx]) << 16;
+}
+
+// ---------------------------------------------------------------------------
+// Flat records
+// ---------------------------------------------------------------------------
+
+template <int kDtype>
+__global__ __launch_bounds__(kThreads)
+void mx9_pack_records_flat(const void* __restrict__ xv, uint64_t nb, uint8_t* __restrict__ packed) {
+    using P = FlatPiece<kDtype>;
+    constexpr int kBlocks = kThreads / P::kLanes;                 // 128 (bf16) or 64 (fp32)
+    __shared__ uint4 stage[kBlocks * kRec / 16];                   // 2304 or 1152 bytes
+    uint8_t* st = reinterpret_cast<uint8_t*>(stage);
+    const uint64_t blk0 = uint64_t(blockIdx.x) * kBlocks;
+    const uint32_t lb = threadIdx.x / P::kLanes, part = threadIdx.x % P::kLanes;
+    const uint64_t blk = blk0 + lb;
+    uint4 d = make_uint4(0u, 0u, 0u, 0u);
+    if (blk < nb) d = reinterpret_cast<const uint4*>(xv)[blk * P::kLanes + part];
+    const P r = pack_flat_piece<kDtype>(d, part);
+    uint8_t* rec = st + kRec * lb;
+    if (part == 0) rec[0] = uint8_t(r.S);
+    if (part == P::kLanes - 1) rec[kRec - 1] = uint8_t(r.prime);
+#pragma unroll
+    for (int k = 0; k < P::kElems; ++k) rec[1 + part * P::kElems + k] = uint8_t(r.qd[k >> 2] >> (8 * (k & 3)));
+    __syncthreads();
+    // the workgroup's records are one contiguous, 16-byte aligned range
+    const uint32_t nbytes = uint32_t(nb - blk0 < uint64_t(kBlocks) ? nb - blk0 : uint64_t(kBlocks)) * kRec;
+    uint8_t* out = packed + blk0 * kRec;
+    for (uint32_t c = threadIdx.x; c * 16u < nbytes; c += kThreads) {
+        if (c * 16u + 16u <= nbytes) {
+            reinterpret_cast<uint4*>(out)[c] = stage[c];
+        } else {
+            for (uint32_t b = c * 16u; b < nbytes; ++b) out[b] = st[b];
+        }
+    }
+}
+
+template <int kOut>
+__global__ __launch_bounds__(kThreads)
+void mx9_unpack_records_flat(const uint8_t* __restrict__ packed, uint64_t nb, void* __restrict__ yv) {
+    constexpr int kLanes = kOut == 0 ? 4 : 2;
+    constexpr int kElems = 16 / kLanes;
+    constexpr int kBlocks = kThreads / kLanes;
+    __shared__ uint4 stage[kBlocks * kRec / 16];
+    uint8_t* st = reinterpret_cast<uint8_t*>(stage);
+    const uint64_t blk0 = uint64_t(blockIdx.x) * kBlocks;
+    const uint32_t nbytes = uint32_t(nb - blk0 < uint64_t(kBlocks) ? nb - blk0 : uint64_t(kBlocks)) * kRec;
+    const uint8_t* in = packed + blk0 * kRec;
+    for (uint32_t c = threadIdx.x; c * 16u < nbytes; c += kThreads) {
+        if (c * 16u + 16u <= nbytes) {
+            stage[c] = reinterpret_cast<const uint4*>(in)[c];
+        } else {
+            for (uint32_t b = c * 16u; b < nbytes; ++b) st[b] = in[b];
+        }
+    }
+    __syncthreads();
+    const uint32_t lb = threadIdx.x / kLanes, part = threadIdx.x % kLanes;
+    const uint64_t blk = blk0 + lb;
+    if (blk >= nb) return;
+    const uint8_t* rec = st + kRec * lb;
+    const uint32_t S = rec[0];
+    const uint32_t pr = uint32_t(rec[kRec - 1]) >> ((kElems / 2) * part);
+    uint32_t qd[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < kElems; ++k) qd[k >> 2] |= uint32_t(rec[1 + part * kElems + k]) << (8 * (k & 3));
+    float y[kElems];
+    unpack_piece<kElems>(qd, S, pr, y);
+    if (kOut == 0) {
+        float4 o = make_float4(y[0], y[1], y[2], y[3]);
+        if (S == 255u) o = make_float4(__uint_as_float(0x7FC00000u), __uint_as_float(0x7FC00000u),
+                                       __uint_as_float(0x7FC00000u), __uint_as_float(0x7FC00000u));
+        reinterpret_cast<float4*>(yv)[blk * kLanes + part] = o;
+    } else {
+        uint4 o = make_uint4(bf16_pair(y[0], y[1]), bf16_pair(y[2], y[3]), bf16_pair(y[4], y[5]), bf16_pair(y[6], y[7]));
+        if (S == 255u) o = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+        reinterpret_cast<uint4*>(yv)[blk * kLanes + part] = o;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Strided: any [outer, len, inner] view, three-part or record output
+// ---------------------------------------------------------------------------
+
+struct StridedView {
+    uint64_t outer, inner;
+    int64_t len;
+    uint32_t nbl;         // blocks per row, ceil(len / 16)
+    uint32_t groups;      // ceil(nbl / kJ)
+    uint64_t nthreads;    // outer * inner * groups
+};
+
+template <int kDtype, bool kRecords, int kJ>
+__global__ __launch_bounds__(kThreads)
+void mx9_pack_strided(const void* __restrict__ xv, StridedView v, int8_t* __restrict__ q,
+                      uint8_t* __restrict__ max_exp, uint8_t* __restrict__ prime,
+                      uint8_t* __restrict__ packed, int64_t ld_p) {
+    const uint64_t t = uint64_t(blockIdx.x) * kThreads + threadIdx.x;
+    if (t >= v.nthreads) return;
+    const uint64_t i = t % v.inner;
+    const uint64_t rest = t / v.inner;
+    const uint32_t g = uint32_t(rest % v.groups);
+    const uint64_t o = rest / v.groups;
+    const uint64_t row = o * v.inner + i;
+    for (int jj = 0; jj < kJ; ++jj) {
+        const uint32_t j = g * kJ + uint32_t(jj);
+        if (j >= v.nbl) break;
+        uint32_t w[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int64_t l = int64_t(16) * j + k;
+            w[k] = l < v.len ? load_bits(xv, (o * uint64_t(v.len) + uint64_t(l)) * v.inner + i, kDtype) : 0u;
+        }
+        uint32_t qd[4], me, pr;
+        pack16(w, qd, me, pr);
+        if (kRecords) {
+            uint8_t* rec = packed + row * uint64_t(ld_p) + uint64_t(kRec) * j;
+            rec[0] = uint8_t(me);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) rec[1 + k] = uint8_t(qd[k >> 2] >> (8 * (k & 3)));
+            rec[kRec - 1] = uint8_t(pr);
+        } else {
+            const uint64_t blk = row * v.nbl + j;
+            reinterpret_cast<uint4*>(q)[blk] = make_uint4(qd[0], qd[1], qd[2], qd[3]);
+            max_exp[blk] = uint8_t(me);
+            prime[blk] = uint8_t(pr);
+        }
+    }
+}
+
+template <int kOut, bool kRecords, int kJ>
+__global__ __launch_bounds__(kThreads)
+void mx9_unpack_strided(const int8_t* __restrict__ q, const uint8_t* __restrict__ max_exp,
+                        const uint8_t* __restrict__ prime, const uint8_t* __restrict__ packed, int64_t ld_p,
+                        StridedView v, void* __restrict__ yv) {
+    const uint64_t t = uint64_t(blockIdx.x) * kThreads + threadIdx.x;
+    if (t >= v.nthreads) return;
+    const uint64_t i = t % v.inner;
+    const uint64_t rest = t / v.inner;
+    const uint32_t g = uint32_t(rest % v.groups);
+    const uint64_t o = rest / v.groups;
+    const uint64_t row = o * v.inner + i;
+    for (int jj = 0; jj < kJ; ++jj) {
+        const uint32_t j = g * kJ + uint32_t(jj);
+        if (j >= v.nbl) break;
+        uint4 qv;
+        uint32_t S, pr;
+        if (kRecords) {
+            const uint8_t* rec = packed + row * uint64_t(ld_p) + uint64_t(kRec) * j;
+            uint32_t qd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int k = 0; k < 16; ++k) qd[k >> 2] |= uint32_t(rec[1 + k]) << (8 * (k & 3));
+            qv = make_uint4(qd[0], qd[1], qd[2], qd[3]);
+            S = rec[0];
+            pr = rec[kRec - 1];
+        } else {
+            const uint64_t blk = row * v.nbl + j;
+            qv = reinterpret_cast<const uint4*>(q)[blk];
+            S = max_exp[blk];
+            pr = prime[blk];
+        }
+        float y[16];
+        unpack16(qv, S, pr, y);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int64_t l = int64_t(16) * j + k;
+            if (l >= v.len) break;
+            const uint64_t idx = (o * uint64_t(v.len) + uint64_t(l)) * v.inner + i;
+            if (kOut == 0) {
+                static_cast<float*>(yv)[idx] = y[k];
+            } else {
+                const uint16_t h = S == 255u ? uint16_t(0x7FC0u) : __builtin_bit_cast(uint16_t, __bf16(y[k]));
+                static_cast<uint16_t*>(yv)[idx] = h;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Axis tiles: 64 * kPer inner positions x 32 / kPer blocks of one o per
+// workgroup.  A lane takes kPer adjacent inner positions (kPer = 2 when the
+// inner extent is even: one 32-bit load carries two bf16 elements, one 64-bit
+// load two fp32 elements).
+// ---------------------------------------------------------------------------
+
+template <int kPer>
+struct Tile {
+    static constexpr int kI = 64 * kPer;                 // inner positions per tile
+    static constexpr int kJ = 32 / kPer;                 // blocks per tile row
+    static constexpr int kJW = kJ / 4;                   // blocks per wave
+    static constexpr int kQPitch = kJ * 16 + 16;         // q row in LDS (bytes)
+    static constexpr int kEPitch = kJ + 4;               // max_exp / prime row in LDS
+    static constexpr int kRPitch = kJ * kRec + 16;       // record row in LDS
+    static constexpr int kQBytes = kI * kQPitch;
+    static constexpr int kLds = kI * kRPitch > kI * (kQPitch + 2 * kEPitch) ? kI * kRPitch : kI * (kQPitch + 2 * kEPitch);
+};
+
+struct AxisTiles {
+    uint64_t outer, inner;
+    int64_t len;
+    uint32_t nbl;         // blocks per row, ceil(len / 16)
+    uint32_t tiles_i;     // ceil(inner / kI)
+    uint32_t tiles_j;     // ceil(nbl / kJ)
+};
+
+struct TileCoord {
+    uint64_t o, i0;
+    uint32_t j0, rows, nj;    // rows: live inner positions, nj: live blocks per row
+};
+
+template <int kPer>
+__device__ __forceinline__ TileCoord tile_coord(const AxisTiles& v) {
+    using T = Tile<kPer>;
+    TileCoord c;
+    // consecutive workgroups take consecutive inner ranges of the same
+    // element rows, so the rows' segments are read (and written) together
+    const uint64_t wg = blockIdx.x;
+    const uint32_t ti = uint32_t(wg % v.tiles_i);
+    const uint64_t rest = wg / v.tiles_i;
+    const uint32_t tj = uint32_t(rest % v.tiles_j);
+    c.o = rest / v.tiles_j;
+    c.i0 = uint64_t(ti) * T::kI;
+    c.j0 = tj * T::kJ;
+    c.rows = uint32_t(v.inner - c.i0 < uint64_t(T::kI) ? v.inner - c.i0 : uint64_t(T::kI));
+    c.nj = v.nbl - c.j0 < uint32_t(T::kJ) ? v.nbl - c.j0 : uint32_t(T::kJ);
+    return c;
+}
+
+// One load of kPer adjacent elements x[idx], x[idx + 1] (idx is even when
+// kPer == 2): a raw word, widened to fp32 bit patterns by raw_elem.
+template <int kDtype, int kPer>
+struct Raw {
+    using type = uint32_t;
+};
+template <>
+struct Raw<0, 2> {
+    using type = uint2;
+};
+
+template <int kDtype, int kPer>
+__device__ __forceinline__ typename Raw<kDtype, kPer>::type load_raw(const void* xv, uint64_t idx) {
+    if constexpr (kDtype == 0 && kPer == 2) {
+        return *reinterpret_cast<const uint2*>(static_cast<const uint32_t*>(xv) + idx);
+    } else if constexpr (kDtype == 1 && kPer == 2) {
+        return *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(xv) + idx);
+    } else {
+        return load_bits(xv, idx, kDtype);
+    }
+}
+
+template <int kDtype, int kPer>
+__device__ __forceinline__ uint32_t raw_elem(typename Raw<kDtype, kPer>::type r, int e) {
+    if constexpr (kDtype == 0 && kPer == 2) {
+        return e == 0 ? r.x : r.y;
+    } else if constexpr (kDtype == 1 && kPer == 2) {
+        return e == 0 ? r << 16 : r & 0xFFFF0000u;
+    } else {
+        return r;
+    }
+}
+
+// Stage one packed block in the tile's LDS row r, block slot jl.
+template <int kPer, bool kRecords>
+__device__ __forceinline__ void stage_block(uint8_t* ls, uint32_t r, uint32_t jl, const uint32_t (&qd)[4],
+                                            uint32_t me, uint32_t pr) {
+    using T = Tile<kPer>;
+    if (kRecords) {
+        uint8_t* rec = ls + r * T::kRPitch + kRec * jl;
+        rec[0] = uint8_t(me);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) rec[1 + k] = uint8_t(qd[k >> 2] >> (8 * (k & 3)));
+        rec[kRec - 1] = uint8_t(pr);
+    } else {
+        *reinterpret_cast<uint4*>(ls + r * T::kQPitch + 16 * jl) = make_uint4(qd[0], qd[1], qd[2], qd[3]);
+        ls[T::kQBytes + r * T::kEPitch + jl] = uint8_t(me);
+        ls[T::kQBytes + T::kI * T::kEPitch + r * T::kEPitch + jl] = uint8_t(pr);
+    }
+}
+
+template <int kDtype, bool kRecords, int kPer>
+__global__ __launch_bounds__(kThreads)
+void mx9_pack_axis_tile(const void* __restrict__ xv, AxisTiles v, int8_t* __restrict__ q,
+                        uint8_t* __restrict__ max_exp, uint8_t* __restrict__ prime,
+                        uint8_t* __restrict__ packed, int64_t ld_p, bool vec_out) {
+    using T = Tile<kPer>;
+    __shared__ uint4 lds[T::kLds / 16];
+    uint8_t* ls = reinterpret_cast<uint8_t*>(lds);
+    const TileCoord c = tile_coord<kPer>(v);
+    const uint32_t il = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const uint32_t r0 = il * kPer;                  // the lane's first row in the tile
+    const bool live_i = r0 < c.rows;                // kPer == 2: rows come in pairs (inner is even)
+    const uint64_t i = c.i0 + r0;
+    // Batches of kU blocks: every load of a batch is issued (predicated, not
+    // branched) before any of its blocks is computed, so 16 * kU loads per
+    // lane are in flight.
+    using RawT = typename Raw<kDtype, kPer>::type;
+    constexpr int kU = 4;
+    static_assert(T::kJW % kU == 0, "batches divide the wave's blocks");
+#pragma unroll 1
+    for (int b0 = 0; b0 < T::kJW; b0 += kU) {
+        const uint32_t jl0 = wave * T::kJW + uint32_t(b0);
+        if (jl0 >= c.nj) break;                     // uniform across the wave
+        RawT raw[kU][16];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t l0 = int64_t(16) * (c.j0 + jl0 + u);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int64_t l = l0 + k;
+                raw[u][k] = RawT{};
+                if (live_i && jl0 + u < c.nj && l < v.len)
+                    raw[u][k] = load_raw<kDtype, kPer>(xv, (c.o * uint64_t(v.len) + uint64_t(l)) * v.inner + i);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            if (jl0 + u >= c.nj) break;
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) {
+                uint32_t w[16];
+#pragma unroll
+                for (int k = 0; k < 16; ++k) w[k] = raw_elem<kDtype, kPer>(raw[u][k], e);
+                uint32_t qd[4], me, pr;
+                pack16(w, qd, me, pr);
+                stage_block<kPer, kRecords>(ls, r0 + e, jl0 + u, qd, me, pr);
+            }
+        }
+    }
+    __syncthreads();
+    const uint64_t row0 = c.o * v.inner + c.i0;      // output row of the tile's first inner position
+    if (kRecords) {
+        const uint32_t rb = kRec * c.nj;            // record bytes per row
+        const uint32_t chunks = (rb + 15) / 16;
+        for (uint32_t t = threadIdx.x; t < c.rows * chunks; t += kThreads) {
+            const uint32_t r = t / chunks, k = t - r * chunks;
+            uint8_t* dst = packed + (row0 + r) * uint64_t(ld_p) + uint64_t(kRec) * c.j0 + 16u * k;
+            const uint8_t* src = ls + r * T::kRPitch + 16u * k;
+            const uint32_t n = rb - 16u * k < 16u ? rb - 16u * k : 16u;
+            if (vec_out && n == 16u) {
+                *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+            } else {
+                for (uint32_t b = 0; b < n; ++b) dst[b] = src[b];
+            }
+        }
+    } else {
+        const uint8_t* ls_e = ls + T::kQBytes;
+        const uint8_t* ls_p = ls_e + T::kI * T::kEPitch;
+        for (uint32_t t = threadIdx.x; t < c.rows * c.nj; t += kThreads) {
+            const uint32_t r = t / c.nj, k = t - r * c.nj;
+            const uint64_t blk = (row0 + r) * v.nbl + c.j0 + k;
+            reinterpret_cast<uint4*>(q)[blk] = *reinterpret_cast<const uint4*>(ls + r * T::kQPitch + 16u * k);
+            max_exp[blk] = ls_e[r * T::kEPitch + k];
+            prime[blk] = ls_p[r * T::kEPitch + k];
+        }
+    }
+}
+
+// Store kPer consecutive outputs y[idx], y[idx + 1] (idx is even when kPer == 2);
+// an element of a poisoned block (nan[e]) is the quiet NaN.
+template <int kOut, int kPer>
+__device__ __forceinline__ void store_run(void* yv, uint64_t idx, const float (&y)[kPer], const bool (&nan)[kPer]) {
+    if (kOut == 0) {
+        uint32_t b[kPer];
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) b[e] = nan[e] ? 0x7FC00000u : __float_as_uint(y[e]);
+        if (kPer == 1) static_cast<uint32_t*>(yv)[idx] = b[0];
+        else *reinterpret_cast<uint2*>(static_cast<uint32_t*>(yv) + idx) = make_uint2(b[0], b[kPer - 1]);
+    } else {
+        uint16_t h[kPer];
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) h[e] = nan[e] ? uint16_t(0x7FC0u) : __builtin_bit_cast(uint16_t, __bf16(y[e]));
+        if (kPer == 1) static_cast<uint16_t*>(yv)[idx] = h[0];
+        else *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(yv) + idx) = uint32_t(h[0]) | (uint32_t(h[kPer - 1]) << 16);
+    }
+}
+
+template <int kOut, bool kRecords, int kPer>
+__global__ __launch_bounds__(kThreads)
+void mx9_unpack_axis_tile(const int8_t* __restrict__ q, const uint8_t* __restrict__ max_exp,
+                          const uint8_t* __restrict__ prime, const uint8_t* __restrict__ packed, int64_t ld_p,
+                          AxisTiles v, void* __restrict__ yv, bool vec_in) {
+    using T = Tile<kPer>;
+    __shared__ uint4 lds[T::kLds / 16];
+    uint8_t* ls = reinterpret_cast<uint8_t*>(lds);
+    uint8_t* ls_e = ls + T::kQBytes;
+    uint8_t* ls_p = ls_e + T::kI * T::kEPitch;
+    const TileCoord c = tile_coord<kPer>(v);
+    const uint64_t row0 = c.o * v.inner + c.i0;
+    if (kRecords) {
+        const uint32_t rb = kRec * c.nj;
+        const uint32_t chunks = (rb + 15) / 16;
+        for (uint32_t t = threadIdx.x; t < c.rows * chunks; t += kThreads) {
+            const uint32_t r = t / chunks, k = t - r * chunks;
+            const uint8_t* src = packed + (row0 + r) * uint64_t(ld_p) + uint64_t(kRec) * c.j0 + 16u * k;
+            uint8_t* dst = ls + r * T::kRPitch + 16u * k;
+            const uint32_t n = rb - 16u * k < 16u ? rb - 16u * k : 16u;
+            if (vec_in && n == 16u) {
+                *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+            } else {
+                for (uint32_t b = 0; b < n; ++b) dst[b] = src[b];
+            }
+        }
+    } else {
+        for (uint32_t t = threadIdx.x; t < c.rows * c.nj; t += kThreads) {
+            const uint32_t r = t / c.nj, k = t - r * c.nj;
+            const uint64_t blk = (row0 + r) * v.nbl + c.j0 + k;
+            *reinterpret_cast<uint4*>(ls + r * T::kQPitch + 16u * k) = reinterpret_cast<const uint4*>(q)[blk];
+            ls_e[r * T::kEPitch + k] = max_exp[blk];
+            ls_p[r * T::kEPitch + k] = prime[blk];
+        }
+    }
+    __syncthreads();
+    const uint32_t il = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const uint32_t r0 = il * kPer;
+    if (r0 >= c.rows) return;                       // no barrier follows
+    const uint64_t i = c.i0 + r0;
+#pragma unroll 2
+    for (int b = 0; b < T::kJW; ++b) {
+        const uint32_t jl = wave * T::kJW + uint32_t(b);
+        if (jl >= c.nj) break;
+        float y[kPer][16];
+        bool nan[kPer];
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const uint32_t r = r0 + e;
+            uint4 qv;
+            uint32_t S, pr;
+            if (kRecords) {
+                const uint8_t* rec = ls + r * T::kRPitch + kRec * jl;
+                uint32_t qd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int k = 0; k < 16; ++k) qd[k >> 2] |= uint32_t(rec[1 + k]) << (8 * (k & 3));
+                qv = make_uint4(qd[0], qd[1], qd[2], qd[3]);
+                S = rec[0];
+                pr = rec[kRec - 1];
+            } else {
+                qv = *reinterpret_cast<const uint4*>(ls + r * T::kQPitch + 16 * jl);
+                S = ls_e[r * T::kEPitch + jl];
+                pr = ls_p[r * T::kEPitch + jl];
+            }
+            unpack16(qv, S, pr, y[e]);
+            nan[e] = S == 255u;
+        }
+        const int64_t l0 = int64_t(16) * (c.j0 + jl);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int64_t l = l0 + k;
+            if (l >= v.len) break;
+            const uint64_t idx = (c.o * uint64_t(v.len) + uint64_t(l)) * v.inner + i;
+            float run[kPer];
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) run[e] = y[e][k];
+            store_run<kOut, kPer>(yv, idx, run, nan);
+        }
+    }
+}
+
+AxisTiles make_tiles(int64_t outer, int64_t len, int64_t inner, int per) {
+    AxisTiles v;
+    v.outer = uint64_t(outer);
+    v.inner = uint64_t(inner);
+    v.len = len;
+    v.nbl = uint32_t((len + 15) / 16);
+    const int ti = 64 * per, tj = 32 / per;
+    v.tiles_i = uint32_t((inner + ti - 1) / ti);
+    v.tiles_j = (v.nbl + uint32_t(tj) - 1) / uint32_t(tj);
+    return v;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+StridedView make_view(int64_t outer, int64_t len, int64_t inner, int kJ) {
+    StridedView v;
+    v.outer = uint64_t(outer);
+    v.inner = uint64_t(inner);
+    v.len = len;
+    v.nbl = uint32_t((len + 15) / 16);
+    v.groups = (v.nbl + uint32_t(kJ) - 1) / uint32_t(kJ);
+    v.nthreads = v.outer * v.inner * v.groups;
+    return v;
+}
+
+dim3 grid_for(uint64_t nthreads) { return dim3(uint32_t((nthreads + kThreads - 1) / kThreads)); }
+
+// kPer = 2 needs an even inner extent (then a lane's two inner positions are
+// one aligned 32- or 64-bit word of every element row).
+inline int per_lane(int64_t inner, const void* buf, int esz) {
+    return inner % 2 == 0 && (reinterpret_cast<uintptr_t>(buf) & uintptr_t(2 * esz - 1)) == 0 ? 2 : 1;
+}
+
+template <bool kRecords>
+void launch_pack_tiles(const void* x, int dtype, int64_t outer, int64_t len, int64_t inner, int8_t* q,
+                       uint8_t* max_exp, uint8_t* prime, uint8_t* packed, int64_t ld_p, hipStream_t stream) {
+    const int per = per_lane(inner, x, dtype == 0 ? 4 : 2);
+    const AxisTiles v = make_tiles(outer, len, inner, per);
+    const dim3 grid(uint32_t(v.outer * v.tiles_i * v.tiles_j));
+    const bool vec = aligned16(packed) && ld_p % 16 == 0;
+    if (dtype == 0 && per == 2) hipLaunchKernelGGL((mx9_pack_axis_tile<0, kRecords, 2>), grid, dim3(kThreads), 0, stream, x, v, q, max_exp, prime, packed, ld_p, vec);
+    else if (dtype == 0) hipLaunchKernelGGL((mx9_pack_axis_tile<0, kRecords, 1>), grid, dim3(kThreads), 0, stream, x, v, q, max_exp, prime, packed, ld_p, vec);
+    else if (per == 2) hipLaunchKernelGGL((mx9_pack_axis_tile<1, kRecords, 2>), grid, dim3(kThreads), 0, stream, x, v, q, max_exp, prime, packed, ld_p, vec);
+    else hipLaunchKernelGGL((mx9_pack_axis_tile<1, kRecords, 1>), grid, dim3(kThreads), 0, stream, x, v, q, max_exp, prime, packed, ld_p, vec);
+}
+
+template <bool kRecords>
+void launch_unpack_tiles(const int8_t* q, const uint8_t* max_exp, const uint8_t* prime, const uint8_t* packed,
+                         int64_t ld_p, int64_t outer, int64_t len, int64_t inner, int out_dtype, void* y,
+                         hipStream_t stream) {
+    const int per = per_lane(inner, y, out_dtype == 0 ? 4 : 2);
+    const AxisTiles v = make_tiles(outer, len, inner, per);
+    const dim3 grid(uint32_t(v.outer * v.tiles_i * v.tiles_j));
+    const bool vec = aligned16(packed) && ld_p % 16 == 0;
+    if (out_dtype == 0 && per == 2) hipLaunchKernelGGL((mx9_unpack_axis_tile<0, kRecords, 2>), grid, dim3(kThreads), 0, stream, q, max_exp, prime, packed, ld_p, v, y, vec);
+    else if (out_dtype == 0) hipLaunchKernelGGL((mx9_unpack_axis_tile<0, kRecords, 1>), grid, dim3(kThreads), 0, stream, q, max_exp, prime, packed, ld_p, v, y, vec);
+    else if (per == 2) hipLaunchKernelGGL((mx9_unpack_axis_tile<1, kRecords, 2>), grid, dim3(kThreads), 0, stream, q, max_exp, prime, packed, ld_p, v, y, vec);
+    else hipLaunchKernelGGL((mx9_unpack_axis_tile<1, kRecords, 1>), grid, dim3(kThreads), 0, stream, q, max_exp, prime, packed, ld_p, v, y, vec);
+}
+
+// Records of a last-axis pack with a pitch or a ragged row: one thread per block.
+void launch_pack_records_rows(const void* x, int dtype, int64_t rows, int64_t len, uint8_t* packed, int64_t ld_p,
+                              hipStream_t stream) {
+    const StridedView v = make_view(rows, len, 1, 1);
+    if (dtype == 0) hipLaunchKernelGGL((mx9_pack_strided<0, true, 1>), grid_for(v.nthreads), dim3(kThreads), 0, stream, x, v, nullptr, nullptr, nullptr, packed, ld_p);
+    else hipLaunchKernelGGL((mx9_pack_strided<1, true, 1>), grid_for(v.nthreads), dim3(kThreads), 0, stream, x, v, nullptr, nullptr, nullptr, packed, ld_p);
+}
+
+void launch_unpack_records_rows(const uint8_t* packed, int64_t ld_p, int64_t rows, int64_t len, int out_dtype,
+                                void* y, hipStream_t stream) {
+    const StridedView v = make_view(rows, len, 1, 1);
+    if (out_dtype == 0) hipLaunchKernelGGL((mx9_unpack_strided<0, true, 1>), grid_for(v.nthreads), dim3(kThreads), 0, stream, nullptr, nullptr, nullptr, packed, ld_p, v, y);
+    else hipLaunchKernelGGL((mx9_unpack_strided<1, true, 1>), grid_for(v.nthreads), dim3(kThreads), 0, stream, nullptr, nullptr, nullptr, packed, ld_p, v, y);
+}
+
+}  // namespace
+
+hipError_t launch_mx9_pack_axis(const void* x, int dtype, int64_t outer, int64_t len, int64_t inner,
+                                int8_t* q, uint8_t* max_exp, uint8_t* prime, hipStream_t stream) {
+    if (inner == 1)   // the last axis: rows of len elements
+        return launch_mx9_pack(x, dtype, outer, len, len, q, max_exp, prime, stream);
+    launch_pack_tiles<false>(x, dtype, outer, len, inner, q, max_exp, prime, nullptr, 0, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx9_unpack_axis(const int8_t* q, const uint8_t* max_exp, const uint8_t* prime,
+                                  int64_t outer, int64_t len, int64_t inner, int out_dtype, void* y,
+                                  hipStream_t stream) {
+    if (inner == 1)
+        return launch_mx9_unpack(q, max_exp, prime, outer, len, out_dtype, y, len, stream);
+    launch_unpack_tiles<false>(q, max_exp, prime, nullptr, 0, outer, len, inner, out_dtype, y, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx9_pack_records(const void* x, int dtype, int64_t outer, int64_t len, int64_t inner,
+                                   uint8_t* packed, int64_t ld_p, hipStream_t stream) {
+    const int64_t nbl = (len + 15) / 16;
+    if (inner == 1 && len % 16 == 0 && ld_p == kRec * nbl && aligned16(x) && aligned16(packed)) {
+        const uint64_t nb = uint64_t(outer) * uint64_t(nbl);
+        const uint32_t per_wg = dtype == 0 ? 64u : 128u;
+        const dim3 grid(uint32_t((nb + per_wg - 1) / per_wg));
+        if (dtype == 0) hipLaunchKernelGGL(mx9_pack_records_flat<0>, grid, dim3(kThreads), 0, stream, x, nb, packed);
+        else hipLaunchKernelGGL(mx9_pack_records_flat<1>, grid, dim3(kThreads), 0, stream, x, nb, packed);
+        return hipGetLastError();
+    }
+    if (inner == 1) launch_pack_records_rows(x, dtype, outer, len, packed, ld_p, stream);
+    else launch_pack_tiles<true>(x, dtype, outer, len, inner, nullptr, nullptr, nullptr, packed, ld_p, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx9_unpack_records(const uint8_t* packed, int64_t ld_p, int64_t outer, int64_t len,
+                                     int64_t inner, int out_dtype, void* y, hipStream_t stream) {
+    const int64_t nbl = (len + 15) / 16;
+    if (inner == 1 && len % 16 == 0 && ld_p == kRec * nbl && aligned16(packed) && aligned16(y)) {
+        const uint64_t nb = uint64_t(outer) * uint64_t(nbl);
+        const uint32_t per_wg = out_dtype == 0 ? 64u : 128u;
+        const dim3 grid(uint32_t((nb + per_wg - 1) / per_wg));
+        if (out_dtype == 0) hipLaunchKernelGGL(mx9_unpack_records_flat<0>, grid, dim3(kThreads), 0, stream, packed, nb, y);
+        else hipLaunchKernelGGL(mx9_unpack_records_flat<1>, grid, dim3(kThreads), 0, stream, packed, nb, y);
+        return hipGetLastError();
+    }
+    if (inner == 1) launch_unpack_records_rows(packed, ld_p, outer, len, out_dtype, y, stream);
+    else launch_unpack_tiles<true>(nullptr, nullptr, nullptr, packed, ld_p, outer, len, inner, out_dtype, y, stream);
+    return hipGetLastError();
+}
+
+}  // namespace mxq

@@ -61,6 +61,20 @@ int check_dual(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x, int32_t bl
     return MX_OK;
 }
 
+// Shared checks of the axis and record calls; nb receives the block count.
+int check_mx9_view(int32_t dtype, int64_t outer, int64_t len, int64_t inner, int32_t block_size,
+                   uint64_t* nb) {
+    if (dtype != MX_DTYPE_F32 && dtype != MX_DTYPE_BF16) return MX_E_DTYPE;
+    if (block_size != 16) return MX_E_BLOCK;
+    if (outer < 0 || len < 0 || inner < 0 || len > kMaxDim || outer > kMaxDim || inner > kMaxDim)
+        return MX_E_SHAPE;
+    const uint64_t elems = uint64_t(outer) * uint64_t(len) * uint64_t(inner);
+    if (elems > (uint64_t(1) << 40)) return MX_E_SHAPE;
+    *nb = uint64_t(outer) * uint64_t(inner) * uint64_t((len + 15) / 16);
+    if (*nb > kMaxThreads) return MX_E_SHAPE;
+    return MX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -163,6 +177,84 @@ int mx9_unpack(const int8_t* q, const uint8_t* max_exp, const uint8_t* prime,
     if (nb == 0) return MX_OK;
     hipError_t e = mxq::launch_mx9_unpack(q, max_exp, prime, rows, cols, out_dtype, y, ld_y,
                                           static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+}
+
+
+int mx9_pack_axis(const void* x, int32_t dtype, int64_t outer, int64_t len, int64_t inner,
+                  int32_t block_size, int8_t* q, uint8_t* max_exp, uint8_t* prime, void* stream) {
+    const bool empty = outer == 0 || len == 0 || inner == 0;
+    if (!empty && (!x || !q || !max_exp || !prime)) return MX_E_NULL;
+    uint64_t nb = 0;
+    int rc = check_mx9_view(dtype, outer, len, inner, block_size, &nb);
+    if (rc != MX_OK) return rc;
+    const uint64_t esz = dtype == MX_DTYPE_F32 ? 4 : 2;
+    if (!empty && (!aligned(x, uintptr_t(esz)) || !aligned(q, 16))) return MX_E_ALIGN;
+    const Span s[4] = {{addr(x), uint64_t(outer) * uint64_t(len) * uint64_t(inner) * esz}, {addr(q), nb * 16},
+                       {addr(max_exp), nb}, {addr(prime), nb}};
+    if (any_overlap(s, 4)) return MX_E_OVERLAP;
+    if (nb == 0) return MX_OK;
+    hipError_t e = mxq::launch_mx9_pack_axis(x, dtype, outer, len, inner, q, max_exp, prime,
+                                             static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+}
+
+int mx9_unpack_axis(const int8_t* q, const uint8_t* max_exp, const uint8_t* prime, int64_t outer,
+                    int64_t len, int64_t inner, int32_t block_size, int32_t out_dtype, void* y,
+                    void* stream) {
+    const bool empty = outer == 0 || len == 0 || inner == 0;
+    if (!empty && (!q || !max_exp || !prime || !y)) return MX_E_NULL;
+    uint64_t nb = 0;
+    int rc = check_mx9_view(out_dtype, outer, len, inner, block_size, &nb);
+    if (rc != MX_OK) return rc;
+    const uint64_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
+    if (!empty && (!aligned(q, 16) || !aligned(y, uintptr_t(esz)))) return MX_E_ALIGN;
+    const Span s[4] = {{addr(q), nb * 16}, {addr(max_exp), nb}, {addr(prime), nb},
+                       {addr(y), uint64_t(outer) * uint64_t(len) * uint64_t(inner) * esz}};
+    if (any_overlap(s, 4)) return MX_E_OVERLAP;
+    if (nb == 0) return MX_OK;
+    hipError_t e = mxq::launch_mx9_unpack_axis(q, max_exp, prime, outer, len, inner, out_dtype, y,
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+}
+
+int mx9_pack_records(const void* x, int32_t dtype, int64_t outer, int64_t len, int64_t inner,
+                     int32_t block_size, uint8_t* packed, int64_t ld_p, void* stream) {
+    const bool empty = outer == 0 || len == 0 || inner == 0;
+    if (!empty && (!x || !packed)) return MX_E_NULL;
+    uint64_t nb = 0;
+    int rc = check_mx9_view(dtype, outer, len, inner, block_size, &nb);
+    if (rc != MX_OK) return rc;
+    const int64_t row_bytes = 18 * ((len + 15) / 16);
+    if (ld_p < row_bytes || ld_p > (int64_t(1) << 40)) return MX_E_STRIDE;
+    const uint64_t esz = dtype == MX_DTYPE_F32 ? 4 : 2;
+    if (!empty && !aligned(x, uintptr_t(esz))) return MX_E_ALIGN;
+    const Span s[2] = {{addr(x), uint64_t(outer) * uint64_t(len) * uint64_t(inner) * esz},
+                       {addr(packed), matrix_bytes(outer * inner, row_bytes, ld_p, 1)}};
+    if (any_overlap(s, 2)) return MX_E_OVERLAP;
+    if (nb == 0) return MX_OK;
+    hipError_t e = mxq::launch_mx9_pack_records(x, dtype, outer, len, inner, packed, ld_p,
+                                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+}
+
+int mx9_unpack_records(const uint8_t* packed, int64_t ld_p, int64_t outer, int64_t len, int64_t inner,
+                       int32_t block_size, int32_t out_dtype, void* y, void* stream) {
+    const bool empty = outer == 0 || len == 0 || inner == 0;
+    if (!empty && (!packed || !y)) return MX_E_NULL;
+    uint64_t nb = 0;
+    int rc = check_mx9_view(out_dtype, outer, len, inner, block_size, &nb);
+    if (rc != MX_OK) return rc;
+    const int64_t row_bytes = 18 * ((len + 15) / 16);
+    if (ld_p < row_bytes || ld_p > (int64_t(1) << 40)) return MX_E_STRIDE;
+    const uint64_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
+    if (!empty && !aligned(y, uintptr_t(esz))) return MX_E_ALIGN;
+    const Span s[2] = {{addr(packed), matrix_bytes(outer * inner, row_bytes, ld_p, 1)},
+                       {addr(y), uint64_t(outer) * uint64_t(len) * uint64_t(inner) * esz}};
+    if (any_overlap(s, 2)) return MX_E_OVERLAP;
+    if (nb == 0) return MX_OK;
+    hipError_t e = mxq::launch_mx9_unpack_records(packed, ld_p, outer, len, inner, out_dtype, y,
+                                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
 }
 

@@ -30,4 +30,19 @@ hipError_t launch_mx9_unpack(const int8_t* q, const uint8_t* max_exp, const uint
                              int64_t rows, int64_t cols, int out_dtype, void* y, int64_t ld_y,
                              hipStream_t stream);
 
+// MX9 in blocks of 16 along the middle axis of a contiguous [outer, len,
+// inner] array (all > 0), blocks numbered (o * inner + i) * ceil(len/16) + j.
+hipError_t launch_mx9_pack_axis(const void* x, int dtype, int64_t outer, int64_t len, int64_t inner,
+                                int8_t* q, uint8_t* max_exp, uint8_t* prime, hipStream_t stream);
+hipError_t launch_mx9_unpack_axis(const int8_t* q, const uint8_t* max_exp, const uint8_t* prime,
+                                  int64_t outer, int64_t len, int64_t inner, int out_dtype, void* y,
+                                  hipStream_t stream);
+
+// The same blocks as 18-byte records (exponent byte, q[16], prime byte); the
+// records of one (o, i) form a row, rows at a pitch of ld_p bytes.
+hipError_t launch_mx9_pack_records(const void* x, int dtype, int64_t outer, int64_t len, int64_t inner,
+                                   uint8_t* packed, int64_t ld_p, hipStream_t stream);
+hipError_t launch_mx9_unpack_records(const uint8_t* packed, int64_t ld_p, int64_t outer, int64_t len,
+                                     int64_t inner, int out_dtype, void* y, hipStream_t stream);
+
 }  // namespace mxq

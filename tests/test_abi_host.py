@@ -24,6 +24,7 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["mx_quantize_2d_dual", "mx_quantize_grouped", "mx9_pack", "mx9_unpack",
+                                  "mx9_pack_axis", "mx9_unpack_axis", "mx9_pack_records", "mx9_unpack_records",
                                   "mx_status_string"])
 
 
@@ -98,6 +99,40 @@ def test_mx9_validation_codes():
     assert unpack(ld=10) == 6 and unpack(y=FAKE * 5 + 2) == 7 and unpack(q=FAKE * 2 + 8) == 7
     assert unpack(y=FAKE * 2 + 64) == 8
     assert unpack(cols=0, y=None, q=None, e=None, p=None) == 0
+
+
+def test_mx9_axis_and_record_validation_codes():
+    lib = mxq.library()
+
+    def pack_axis(dtype=1, outer=3, length=40, inner=5, bs=16, x=FAKE, q=FAKE * 2, e=FAKE * 3, p=FAKE * 4):
+        return lib.mx9_pack_axis(x, dtype, outer, length, inner, bs, q, e, p, None)
+
+    def unpack_axis(od=1, outer=3, length=40, inner=5, bs=16, y=FAKE * 5, q=FAKE * 2, e=FAKE * 3, p=FAKE * 4):
+        return lib.mx9_unpack_axis(q, e, p, outer, length, inner, bs, od, y, None)
+
+    def pack_rec(dtype=0, outer=3, length=40, inner=5, bs=16, x=FAKE, pk=FAKE * 2, ld=54):
+        return lib.mx9_pack_records(x, dtype, outer, length, inner, bs, pk, ld, None)
+
+    def unpack_rec(od=0, outer=3, length=40, inner=5, bs=16, y=FAKE * 5, pk=FAKE * 2, ld=54):
+        return lib.mx9_unpack_records(pk, ld, outer, length, inner, bs, od, y, None)
+    # 3 * 5 rows of ceil(40 / 16) = 3 blocks
+    assert pack_axis(x=None) == 1 and pack_axis(dtype=2) == 2 and pack_axis(bs=32) == 3
+    assert pack_axis(inner=-1) == 5 and pack_axis(length=(1 << 30) + 1) == 5
+    assert pack_axis(outer=1 << 20, inner=1 << 20, length=1 << 20) == 5
+    assert pack_axis(x=FAKE + 1) == 7 and pack_axis(q=FAKE * 2 + 8) == 7
+    assert pack_axis(e=FAKE * 2 + 16) == 8                        # max_exp inside q
+    assert pack_axis(outer=0, x=None, q=None, e=None, p=None) == 0
+    assert unpack_axis(y=None) == 1 and unpack_axis(od=5) == 2 and unpack_axis(bs=8) == 3
+    assert unpack_axis(y=FAKE * 5 + 1) == 7 and unpack_axis(q=FAKE * 2 + 4) == 7
+    assert unpack_axis(y=FAKE * 3 - 8) == 8                       # y runs into max_exp
+    assert pack_rec(pk=None) == 1 and pack_rec(dtype=7) == 2 and pack_rec(bs=15) == 3
+    assert pack_rec(ld=53) == 6 and pack_rec(ld=1 << 41) == 6
+    assert pack_rec(x=FAKE + 2) == 7
+    assert pack_rec(pk=FAKE + 64) == 8                            # records inside the input
+    assert pack_rec(length=0, x=None, pk=None) == 0
+    assert unpack_rec(pk=None) == 1 and unpack_rec(od=2) == 2 and unpack_rec(ld=10) == 6
+    assert unpack_rec(y=FAKE * 5 + 2) == 7 and unpack_rec(y=FAKE * 2 + 100) == 8
+    assert unpack_rec(inner=0, y=None, pk=None) == 0
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch):

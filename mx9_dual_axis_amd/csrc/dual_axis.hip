@@ -29,11 +29,13 @@
 //              multiplier) and rounds to nearest even; it does not saturate,
 //              so the colwise Inf block (scale 254) maps its NaN bytes to
 //              +-448 afterwards, and poisoned blocks are overwritten with 0x7F.
-//   * order  : tiles are visited in a diagonal order (consecutive workgroups
-//              take consecutive tile rows, each shifted one tile column), which
-//              spreads the concurrently active row segments of the input and
-//              of both outputs over the HBM channels better than row-major or
-//              column-major order (measured).
+//   * order  : consecutive workgroups take consecutive tile rows.  A call
+//              that moves more than twice the memory-side cache visits the
+//              tiles in a diagonal order (each tile row shifted one tile
+//              column), which spreads the concurrently active row segments of
+//              the input and of both outputs over the HBM channels; a smaller
+//              call goes down whole tile columns (column-major), which the
+//              cache serves better (measured on the workloads' shapes).
 //   * s_row  : a tile owns only 4 scale bytes per row, and 128 scattered 4-byte
 //              stores per tile cost more than the rest of the tile's writes.
 //              When N <= 16256 and N % 512 == 0, each tile instead writes its
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(kThreads)
 void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, int64_t N,
                       uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
                       uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
-                      uint32_t tiles_n, uint32_t tiles, uint32_t row_stream_mask,
+                      uint32_t tiles_n, uint32_t tiles, uint32_t row_stream_mask, bool diagonal,
                       const int32_t* __restrict__ offs, int32_t G, int32_t* __restrict__ err) {
     __shared__ uint4 lds_tile[kTile * 16];     // [128 rows][16 x 16 bytes]
     __shared__ uint32_t lds_srow[kTile];       // the tile's 4 rowwise scale bytes per row
@@ -166,7 +168,7 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
     const uint32_t bid = blockIdx.x;
     const uint32_t tiles_m = tiles / tiles_n;
     const uint32_t tm = bid % tiles_m;
-    const uint32_t tn = (bid / tiles_m + tm) % tiles_n;
+    const uint32_t tn = diagonal ? (bid / tiles_m + tm) % tiles_n : bid / tiles_m;
     const int64_t m0 = int64_t(tm) * kTile;
     const int64_t n0 = int64_t(tn) * kTile;
 
@@ -333,21 +335,22 @@ hipError_t launch_dual_axis(const uint16_t* x, int64_t M, int64_t N, int64_t ld_
     const bool stage = N <= kMaxStagedN && N % 512 == 0;
     // q_row streaming share by the call's size against the memory-side cache
     const double call_bytes = 4.0625 * double(M) * double(N);
-    const uint32_t row_stream = call_bytes > 2.0 * kMemorySideCacheBytes ? 0x3Fu : 0x00u;
+    const bool large = call_bytes > 2.0 * kMemorySideCacheBytes;
+    const uint32_t row_stream = large ? 0x3Fu : 0x00u;
     const int32_t* no_offs = nullptr;
     int32_t* no_err = nullptr;
     if (grouped && stage)
         hipLaunchKernelGGL((dual_axis_kernel<true, true>), dim3(tiles), dim3(kThreads), 0, stream,
-                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles, row_stream, offs, G, err);
+                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles, row_stream, large, offs, G, err);
     else if (grouped)
         hipLaunchKernelGGL((dual_axis_kernel<true, false>), dim3(tiles), dim3(kThreads), 0, stream,
-                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles, row_stream, offs, G, err);
+                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles, row_stream, large, offs, G, err);
     else if (stage)
         hipLaunchKernelGGL((dual_axis_kernel<false, true>), dim3(tiles), dim3(kThreads), 0, stream,
-                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles, row_stream, no_offs, 0, no_err);
+                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles, row_stream, large, no_offs, 0, no_err);
     else
         hipLaunchKernelGGL((dual_axis_kernel<false, false>), dim3(tiles), dim3(kThreads), 0, stream,
-                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles, row_stream, no_offs, 0, no_err);
+                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles, row_stream, large, no_offs, 0, no_err);
     if (stage) {
         const uint32_t lds = uint32_t(N / kTile) * 129u * 4u;
         hipLaunchKernelGGL(srow_permute_kernel, dim3(uint32_t(M / kTile)), dim3(kPermThreads), lds, stream, s_row, N);

@@ -15,6 +15,9 @@ Sources (web pages):
     uncovered-tail rule (PR description).
   * AMD-AGI/ALTO PR #33 "feat: mx9: add fused MX9 quantization kernel with
     pack/unpack" -- the MX9 storage format (Summary, Key design choices).
+  * AMD-AGI/ALTO PR #31 "Add MXFP8 grouped GEMM (E4M3) for routed-expert MoE
+    training" -- the contraction that consumes the MXFP8 outputs (description:
+    E4M3 operands with block-32 E8M0 scales, 1-D cumulative offsets).
 """
 from __future__ import annotations
 
@@ -341,3 +344,81 @@ def mx9_from_records(packed: np.ndarray, rows: int, bpr: int):
     f.restype = None
     f(_ptr(packed), packed.strides[0], rows, bpr, _ptr(q), _ptr(e), _ptr(p))
     return q, e, p
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 block-scaled contraction (ALTO PR #31, the grouped GEMM's arithmetic)
+# ---------------------------------------------------------------------------
+
+def _scale_view(s, rs: int, bs: int):
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    return s, int(rs), int(bs)
+
+
+def mx_gemm_nt(A, sA, B, sB, *, sa_strides, sb_strides, k0: int = 0, k1: int | None = None,
+               rows=None, threads: int = 1, with_abs: bool = False):
+    """C[m][n] = sum_k dec(A[m,k]) 2^(sA(m,k/32)-127) dec(B[n,k]) 2^(sB(n,k/32)-127)
+    over k in [k0, k1), in binary64.  A: uint8 E4M3 codes [M, >=k1] (contraction
+    contiguous), B: [N, >=k1]; sA(m, b) = sA.flat[m * rs + b * bs] with
+    (rs, bs) = sa_strides, likewise sB.  ``rows``: optional (m0, m1) range; the
+    result has M rows either way (rows outside the range are 0).  Returns C
+    (float64 [M, N]) and, with ``with_abs``, the sum of |products| per entry."""
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    M, N = A.shape[0], B.shape[0]
+    k1 = A.shape[1] if k1 is None else int(k1)
+    if k0 % 32 or k1 % 32:
+        raise ValueError("k0 and k1 must be multiples of 32")
+    sA, sa_rs, sa_bs = _scale_view(sA, *sa_strides)
+    sB, sb_rs, sb_bs = _scale_view(sB, *sb_strides)
+    C = np.zeros((M, N), np.float64)
+    absC = np.zeros((M, N), np.float64) if with_abs else None
+    m0, m1 = (0, M) if rows is None else rows
+    f = _load().oref_mx_gemm_nt
+    f.argtypes = [_P, _I64, _P, _I64, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _I64]
+    f.restype = None
+
+    def job(r0, r1):
+        return lambda: f(_ptr(A), A.shape[1], _ptr(sA), sa_rs, sa_bs, _ptr(B), B.shape[1], _ptr(sB), sb_rs, sb_bs,
+                         m0 + r0, m0 + r1, N, k0, k1, _ptr(C), _ptr(absC) if absC is not None else None, N)
+    _run([job(a, b) for a, b in _splits(m1 - m0, threads)], threads)
+    return (C, absC) if with_abs else C
+
+
+def mx_grouped_gemm_rows(A, sA, B, sB, offs, *, sa_strides, sb_strides, threads: int = 1, with_abs: bool = False):
+    """Grouped contraction over row groups (the forward of a routed-expert
+    layer): rows offs[g-1] <= m < offs[g] of A multiply expert g's operand
+    B[g] ([E, N, K] codes, sB[g] its scales); rows from offs[-1] on (the
+    uncovered tail) give 0 (reading: the pages pad the activation buffer and
+    give the padding no expert)."""
+    A = np.asarray(A)
+    M, N = A.shape[0], B.shape[1]
+    C = np.zeros((M, N), np.float64)
+    absC = np.zeros((M, N), np.float64)
+    lo = 0
+    for g, hi in enumerate(np.asarray(offs, dtype=np.int64)):
+        if hi > lo:
+            c, a = mx_gemm_nt(A, sA, B[g], sB[g], sa_strides=sa_strides, sb_strides=sb_strides,
+                              rows=(int(lo), int(hi)), threads=threads, with_abs=True)
+            C[lo:hi] = c[lo:hi]
+            absC[lo:hi] = a[lo:hi]
+        lo = hi
+    return (C, absC) if with_abs else C
+
+
+def mx_grouped_gemm_k(A, sA, B, sB, offs, *, sa_strides, sb_strides, threads: int = 1, with_abs: bool = False):
+    """Grouped contraction over contraction-index groups (the weight
+    gradient of a routed-expert layer): C[g] = sum over offs[g-1] <= k <
+    offs[g] of A[:, k] B[:, k] with their block scales; an empty group gives
+    0.  Returns float64 [G, M, N]."""
+    offs = np.asarray(offs, dtype=np.int64)
+    M, N = np.asarray(A).shape[0], np.asarray(B).shape[0]
+    C = np.zeros((len(offs), M, N), np.float64)
+    absC = np.zeros_like(C)
+    lo = 0
+    for g, hi in enumerate(offs):
+        if hi > lo:
+            C[g], absC[g] = mx_gemm_nt(A, sA, B, sB, sa_strides=sa_strides, sb_strides=sb_strides,
+                                       k0=int(lo), k1=int(hi), threads=threads, with_abs=True)
+        lo = hi
+    return (C, absC) if with_abs else C

@@ -490,3 +490,52 @@ void oref_mx9_from_records(const uint8_t *packed, int64_t ld_p, int64_t rows, in
         }
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* MXFP8 block-scaled contraction   [MXFP8 GG] (AMD-AGI/ALTO PR #31: the     */
+/* E4M3 grouped GEMM whose operands are MXFP8 data with E8M0 block-32       */
+/* scales along the contraction)                                             */
+/* ------------------------------------------------------------------------ */
+
+/* E8M0 scale byte b: 2^(b - 127); 255 is NaN. */
+static double e8m0_value(uint8_t b)
+{
+    return b == 255 ? NAN : ldexp(1.0, (int)b - 127);
+}
+
+/* "NT" form: both operands are stored with the contraction index contiguous.
+ *   C[m][n] = sum over k in [k0, k1) of
+ *             e4m3(A[m][k]) * 2^(sA(m, k/32) - 127) * e4m3(B[n][k]) * 2^(sB(n, k/32) - 127)
+ * with sA(m, b) = sA[m * sa_rs + b * sa_bs] and sB(n, b) = sB[n * sb_rs + b * sb_bs],
+ * for rows m0 <= m < m1 and all n < N; k0 and k1 are multiples of 32.
+ * Each product is exact in binary64 and the sum is accumulated in binary64
+ * in k order.  absC, when non-NULL, receives the sum of |product|: the
+ * quantity any other summation order's rounding error is proportional to.
+ * NaN codes and scale byte 255 propagate as NaN. */
+void oref_mx_gemm_nt(const uint8_t *A, int64_t lda, const uint8_t *sA, int64_t sa_rs, int64_t sa_bs,
+                     const uint8_t *B, int64_t ldb, const uint8_t *sB, int64_t sb_rs, int64_t sb_bs,
+                     int64_t m0, int64_t m1, int64_t N, int64_t k0, int64_t k1,
+                     double *C, double *absC, int64_t ldc)
+{
+    double dec[256], sc[256];
+    int64_t m, n, k;
+    int i;
+    for (i = 0; i < 256; i++) {
+        dec[i] = oref_e4m3_value((uint8_t)i);
+        sc[i] = e8m0_value((uint8_t)i);
+    }
+    for (m = m0; m < m1; m++) {
+        for (n = 0; n < N; n++) {
+            double acc = 0.0, mag = 0.0;
+            for (k = k0; k < k1; k++) {
+                double a = dec[A[m * lda + k]] * sc[sA[m * sa_rs + (k / 32) * sa_bs]];
+                double b = dec[B[n * ldb + k]] * sc[sB[n * sb_rs + (k / 32) * sb_bs]];
+                acc += a * b;
+                mag += fabs(a * b);
+            }
+            C[m * ldc + n] = acc;
+            if (absC)
+                absC[m * ldc + n] = mag;
+        }
+    }
+}

@@ -258,6 +258,75 @@ def measure_configs(dev, launches: int, sets: int = 3):
                                                **summarize(time_rotating(up, launches), rows * cols * elem_b))
         del xs, packs, ys, pk, up
     torch.cuda.synchronize()
+    res.update(measure_gemm(dev, launches))
+    return res
+
+
+PEAK_FP8_TFLOPS = 5000.0
+
+
+def measure_gemm(dev, launches: int):
+    """The consumer contraction on the matrix cores: the routed-expert forward
+    and weight gradient over the grouped activation buffer (its cast outputs,
+    64 experts of 2048 output features), and a dense 8192^3 product.  Rates
+    are useful FLOP/s (2 per multiply-add over the covered rows) against the
+    5.0 PFLOP/s dense E4M3 peak."""
+    import numpy as np
+    import torch
+
+    import mx9_dual_axis_amd as mxq
+    from mx9_dual_axis_amd import synth
+
+    def tsum(ts, flops, workload):
+        ts = sorted(ts)
+        mean = sum(ts) / len(ts)
+        tf = flops / mean / 1e12
+        return {"workload": workload, "us": round(mean * 1e6, 2), "median_us": round(ts[len(ts) // 2] * 1e6, 2),
+                "flop": int(flops), "TFLOP_s": round(tf, 1), "frac": round(tf / PEAK_FP8_TFLOPS, 4)}
+
+    print("bench: MXFP8 contractions (grouped forward, weight gradient, dense)", file=sys.stderr, flush=True)
+    g = np.random.default_rng(11)
+    xb, offs = synth.grouped()
+    Mt, K = xb.shape
+    N, E = 2048, len(offs)
+    covered = int(offs[-1])
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+    od = torch.from_numpy(offs).to(dev)
+    q_row, s_row, q_col, s_col = mxq.mx_quantize_grouped(x, od)
+    del x
+
+    def codes(shape):
+        c = torch.from_numpy(g.integers(0, 256, shape, dtype=np.uint8)).to(dev)
+        return torch.where((c & 0x7F) == 0x7F, torch.full_like(c, 0x38), c)
+
+    def scales(shape):
+        return torch.from_numpy(g.integers(118, 137, shape, dtype=np.uint8)).to(dev)
+
+    res = {}
+    W = codes((E, N, K))
+    sW = scales((E, N, K // 32))
+    out = torch.empty((Mt, N), dtype=torch.bfloat16, device=dev)
+    fwd = [lambda: mxq.mx_grouped_gemm_rows(q_row, s_row, W, sW, od, out=out)]
+    res["gemm_grouped_forward"] = tsum(time_rotating(fwd, launches), 2.0 * covered * N * K,
+                                       f"grouped forward, cast activations [{Mt}, {K}] (64 groups, {covered} rows) "
+                                       f"x 64 experts [{N}, {K}] -> bf16")
+    del W, sW, out, fwd
+    dY = codes((N, Mt))
+    sdY = scales((Mt // 32, N))
+    dW = torch.empty((E, K, N), dtype=torch.bfloat16, device=dev)
+    wg = [lambda: mxq.mx_grouped_gemm_k(q_col, s_col.t(), dY, sdY.t(), od, out=dW)]
+    res["gemm_grouped_wgrad"] = tsum(time_rotating(wg, launches), 2.0 * covered * N * K,
+                                     f"grouped weight gradient, cast q_col [{K}, {Mt}] x dY [{N}, {Mt}] over 64 groups "
+                                     f"-> bf16 [64, {K}, {N}]")
+    del dY, sdY, dW, wg, q_row, s_row, q_col, s_col
+    D = 8192
+    A, B = codes((D, D)), codes((D, D))
+    sA, sB = scales((D, D // 32)), scales((D, D // 32))
+    C = torch.empty((D, D), dtype=torch.bfloat16, device=dev)
+    dn = [lambda: mxq.mx_gemm_nt(A, sA, B, sB, out=C)]
+    res["gemm_dense_8192"] = tsum(time_rotating(dn, launches), 2.0 * D ** 3, "dense [8192, 8192, 8192] -> bf16")
+    del A, B, sA, sB, C, dn
+    torch.cuda.synchronize()
     return res
 
 

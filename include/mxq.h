@@ -7,6 +7,8 @@
  *           quantization with correct metadata".
  *   [MX9]   AMD-AGI/ALTO PR #33, "feat: mx9: add fused MX9 quantization
  *           kernel with pack/unpack".
+ *   [GG]    AMD-AGI/ALTO PR #31, "Add MXFP8 grouped GEMM (E4M3) for
+ *           routed-expert MoE training".
  *
  * Conventions shared by every entry point
  *   - Pointers named x, q*, s*, offs, err, y, max_exp and prime are DEVICE
@@ -224,6 +226,68 @@ int mx9_pack_records(const void *x, int32_t dtype, int64_t outer, int64_t len, i
  */
 int mx9_unpack_records(const uint8_t *packed, int64_t ld_p, int64_t outer, int64_t len, int64_t inner,
                        int32_t block_size, int32_t out_dtype, void *y, void *stream);
+
+/*
+ * mx_gemm_nt -- MXFP8 block-scaled contraction, the consumer of the
+ * dual-axis cast's outputs ([GG], description: E4M3 operands with E8M0
+ * scales per 32 elements of the contraction).
+ *
+ *   C[m][n] = sum_k e4m3(A[m][k]) 2^(sA(m, k/32) - 127) e4m3(B[n][k]) 2^(sB(n, k/32) - 127)
+ *
+ *   A      E4M3 codes [M, K], contraction contiguous, row pitch lda bytes
+ *          (q_row of the cast, or q_col for a contraction over tokens).
+ *   sA     E8M0 bytes, sA(m, b) = sA[m * sa_rs + b * sa_bs]: (K/32, 1) for the
+ *          cast's s_row, (1, M) for its s_col read as the scales of q_col.
+ *   B, sB  the same for the second operand, [N, K] with pitch ldb.
+ *   C      [M, N], fp32 (out_dtype MX_DTYPE_F32) or bf16 (MX_DTYPE_BF16,
+ *          nearest-even), row pitch ldc elements; computed on the matrix
+ *          cores with fp32 accumulation (summation order unspecified).
+ *   M, N, K multiples of 128 (at most 2^24); lda, ldb multiples of 16.
+ *
+ * Errors: MX_E_NULL, MX_E_DTYPE (out_dtype), MX_E_SHAPE, MX_E_STRIDE (a pitch
+ * below its row or misaligned, a negative scale stride), MX_E_ALIGN (A or B
+ * not 16-byte aligned, C not aligned to its element), MX_E_OVERLAP (C
+ * overlaps an input).  M == 0 or N == 0 is a no-op.
+ */
+int mx_gemm_nt(const uint8_t *A, int64_t lda, const uint8_t *sA, int64_t sa_rs, int64_t sa_bs,
+               const uint8_t *B, int64_t ldb, const uint8_t *sB, int64_t sb_rs, int64_t sb_bs,
+               int64_t M, int64_t N, int64_t K, void *C, int64_t ldc, int32_t out_dtype, void *stream);
+
+/*
+ * mx_grouped_gemm_rows -- the routed-expert forward ([GG]: 1-D cumulative
+ * offsets over a padded activation buffer, one weight operand per expert).
+ * Rows offs[g-1] <= m < offs[g] of A (offs[-1] = 0) are contracted with
+ * expert g's operand B + g * b_gs (codes [N, K], pitch ldb) and its scales
+ * sB + g * sb_gs; rows m >= offs[G-1] (the uncovered tail) give 0 (reading:
+ * the padding belongs to no expert).  offs (device int32 [G], G >= 1) must
+ * satisfy the grouped cast's rule (ascending multiples of 128 within
+ * [0, M]); otherwise the rows' expert is unspecified but every access stays
+ * inside the operands.  Other arguments and errors as for mx_gemm_nt, plus
+ * MX_E_SHAPE for G < 1, MX_E_NULL for offs NULL, MX_E_STRIDE for a negative
+ * group stride.
+ */
+int mx_grouped_gemm_rows(const uint8_t *A, int64_t lda, const uint8_t *sA, int64_t sa_rs, int64_t sa_bs,
+                         const uint8_t *B, int64_t ldb, int64_t b_gs, const uint8_t *sB, int64_t sb_rs,
+                         int64_t sb_bs, int64_t sb_gs, const int32_t *offs, int32_t G, int64_t M, int64_t N,
+                         int64_t K, void *C, int64_t ldc, int32_t out_dtype, void *stream);
+
+/*
+ * mx_grouped_gemm_k -- the routed-expert weight gradient: the contraction
+ * runs over the token axis, grouped by the same offsets.  Group g writes
+ * C + g * c_gs ([M, N], pitch ldc, elements) with the sum over
+ * offs[g-1] <= k < offs[g]; an empty group writes 0; k >= offs[G-1] is not
+ * read.  A [M, K] and B [N, K] hold the contraction contiguous (the cast's
+ * q_col of the two token-major operands), sA and sB their scales (the
+ * cast's s_col, as (1, M) and (1, N) strided views).  Invalid offsets are
+ * clamped to multiples of 128 inside [0, K]: the results are then
+ * unspecified, the accesses stay inside the operands.  Errors as for
+ * mx_gemm_nt, plus MX_E_SHAPE (G < 1, or more than 2^31 tiles),
+ * MX_E_STRIDE (c_gs smaller than one group's C).
+ */
+int mx_grouped_gemm_k(const uint8_t *A, int64_t lda, const uint8_t *sA, int64_t sa_rs, int64_t sa_bs,
+                      const uint8_t *B, int64_t ldb, const uint8_t *sB, int64_t sb_rs, int64_t sb_bs,
+                      const int32_t *offs, int32_t G, int64_t M, int64_t N, int64_t K, void *C, int64_t ldc,
+                      int64_t c_gs, int32_t out_dtype, void *stream);
 
 /* Host function: a static, human-readable name for an mx_status value. */
 const char *mx_status_string(int status);

@@ -13,6 +13,8 @@ Entry points (same names as the C ABI):
   mx9_unpack(q, max_exp, prime, rows, cols, out_dtype) -> y
   mx9_pack_axis(x, axis) / mx9_unpack_axis(q, max_exp, prime, shape, axis)
   mx9_pack_records(x, axis) -> packed uint8 / mx9_unpack_records(packed, shape, axis)
+  mx_gemm_nt(A, sA, B, sB)                -> C = A B^T (MXFP8 operands)
+  mx_grouped_gemm_rows(A, sA, B, sB, offs) / mx_grouped_gemm_k(A, sA, B, sB, offs)
 plus the signatures the pages use: ``mxfp8_quantize_2d_1x32_32x1`` (dense
 when ``offs`` is None, grouped otherwise), ``convert_to_mx9`` and
 ``convert_from_mx9`` (with an axis), and their single-tensor forms
@@ -61,8 +63,14 @@ def _load():
     lib.mx9_unpack_axis.argtypes = [P, P, P, I64, I64, I64, I32, I32, P, P]
     lib.mx9_pack_records.argtypes = [P, I32, I64, I64, I64, I32, P, I64, P]
     lib.mx9_unpack_records.argtypes = [P, I64, I64, I64, I64, I32, I32, P, P]
+    lib.mx_gemm_nt.argtypes = [P, I64, P, I64, I64, P, I64, P, I64, I64, I64, I64, I64, P, I64, I32, P]
+    lib.mx_grouped_gemm_rows.argtypes = [P, I64, P, I64, I64, P, I64, I64, P, I64, I64, I64, P, I32, I64, I64, I64,
+                                         P, I64, I32, P]
+    lib.mx_grouped_gemm_k.argtypes = [P, I64, P, I64, I64, P, I64, P, I64, I64, P, I32, I64, I64, I64, P, I64, I64,
+                                      I32, P]
     for f in (lib.mx_quantize_2d_dual, lib.mx_quantize_grouped, lib.mx9_pack, lib.mx9_unpack,
-              lib.mx9_pack_axis, lib.mx9_unpack_axis, lib.mx9_pack_records, lib.mx9_unpack_records):
+              lib.mx9_pack_axis, lib.mx9_unpack_axis, lib.mx9_pack_records, lib.mx9_unpack_records,
+              lib.mx_gemm_nt, lib.mx_grouped_gemm_rows, lib.mx_grouped_gemm_k):
         f.restype = ctypes.c_int
     lib.mx_status_string.argtypes = [ctypes.c_int]
     lib.mx_status_string.restype = ctypes.c_char_p
@@ -313,6 +321,97 @@ def mx9_unpack_records(packed: torch.Tensor, shape, axis: int = -1, out_dtype=to
     _check(_load().mx9_unpack_records(packed.data_ptr(), packed.stride(0), outer, length, inner, block_size, od,
                                       y.data_ptr(), _stream(packed.device)))
     return y
+
+
+def _codes(t: torch.Tensor, name: str):
+    _need_cuda(t, name)
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn) or t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D E4M3 codes (uint8 or float8_e4m3fn) with contiguous rows")
+
+
+def _scales(s: torch.Tensor, rows: int, k: int, name: str):
+    """(rs, bs) of a [rows, k/32] uint8 scale view with any strides."""
+    _need_cuda(s, name)
+    if s.dtype != torch.uint8 or s.dim() != 2 or tuple(s.shape) != (rows, k // 32):
+        raise ValueError(f"{name} must be a uint8 [{rows}, {k // 32}] view (any strides)")
+    return s.stride(0), s.stride(1)
+
+
+def _gemm_out(out, shape, out_dtype, dev):
+    if out is None:
+        return torch.empty(shape, dtype=out_dtype, device=dev)
+    if tuple(out.shape) != tuple(shape) or out.stride(-1) != 1:
+        raise ValueError(f"out must be {tuple(shape)} with contiguous rows")
+    return out
+
+
+def mx_gemm_nt(A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB: torch.Tensor, out_dtype=torch.float32,
+               out: torch.Tensor | None = None):
+    """C = A B^T with MXFP8 operands: A [M, K] and B [N, K] E4M3 codes
+    (contraction contiguous), sA [M, K/32] and sB [N, K/32] E8M0 scale views
+    (e.g. the cast's s_row, or s_col.t() for q_col operands).  C is float32
+    or bfloat16 [M, N]."""
+    _codes(A, "A")
+    _codes(B, "B")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("A and B must share the contraction extent")
+    sa, sb = _scales(sA, M, K, "sA"), _scales(sB, N, K, "sB")
+    C = _gemm_out(out, (M, N), out_dtype, A.device)
+    od = _out_code(C.dtype)
+    _check(_load().mx_gemm_nt(A.data_ptr(), A.stride(0), sA.data_ptr(), sa[0], sa[1], B.data_ptr(), B.stride(0),
+                              sB.data_ptr(), sb[0], sb[1], M, N, K, C.data_ptr(), C.stride(0), od,
+                              _stream(A.device)))
+    return C
+
+
+def mx_grouped_gemm_rows(A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB: torch.Tensor, offs: torch.Tensor,
+                         out_dtype=torch.float32, out: torch.Tensor | None = None):
+    """Routed-expert forward: rows of group g (cumulative int32 offs) use
+    expert g's B[g] ([E, N, K] codes) and sB[g] ([E, N, K/32] view); rows
+    past offs[-1] give 0."""
+    _codes(A, "A")
+    M, K = A.shape
+    if B.dim() != 3 or B.stride(2) != 1 or B.shape[2] != K:
+        raise ValueError("B must be [E, N, K] codes with contiguous rows")
+    E, N = B.shape[0], B.shape[1]
+    if sB.dim() != 3 or tuple(sB.shape) != (E, N, K // 32) or sB.dtype != torch.uint8:
+        raise ValueError("sB must be a uint8 [E, N, K/32] view")
+    if offs.dtype != torch.int32 or offs.dim() != 1 or not offs.is_contiguous() or offs.numel() > E:
+        raise ValueError("offs must be a contiguous int32 [G] tensor with G <= E")
+    _need_cuda(offs, "offs")
+    sa = _scales(sA, M, K, "sA")
+    C = _gemm_out(out, (M, N), out_dtype, A.device)
+    _check(_load().mx_grouped_gemm_rows(A.data_ptr(), A.stride(0), sA.data_ptr(), sa[0], sa[1], B.data_ptr(),
+                                        B.stride(1), B.stride(0), sB.data_ptr(), sB.stride(1), sB.stride(2),
+                                        sB.stride(0), offs.data_ptr(), offs.numel(), M, N, K, C.data_ptr(),
+                                        C.stride(0), _out_code(C.dtype), _stream(A.device)))
+    return C
+
+
+def mx_grouped_gemm_k(A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB: torch.Tensor, offs: torch.Tensor,
+                      out_dtype=torch.float32, out: torch.Tensor | None = None):
+    """Routed-expert weight gradient: C[g] = A[:, r_g] B[:, r_g]^T over the
+    contraction range r_g = [offs[g-1], offs[g]).  A [M, K], B [N, K] codes,
+    sA [M, K/32], sB [N, K/32] views (the cast's s_col.t()).  Returns
+    [G, M, N]."""
+    _codes(A, "A")
+    _codes(B, "B")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("A and B must share the contraction extent")
+    if offs.dtype != torch.int32 or offs.dim() != 1 or not offs.is_contiguous():
+        raise ValueError("offs must be a contiguous int32 [G] tensor")
+    _need_cuda(offs, "offs")
+    G = offs.numel()
+    sa, sb = _scales(sA, M, K, "sA"), _scales(sB, N, K, "sB")
+    C = _gemm_out(out, (G, M, N), out_dtype, A.device)
+    _check(_load().mx_grouped_gemm_k(A.data_ptr(), A.stride(0), sA.data_ptr(), sa[0], sa[1], B.data_ptr(),
+                                     B.stride(0), sB.data_ptr(), sb[0], sb[1], offs.data_ptr(), G, M, N, K,
+                                     C.data_ptr(), C.stride(1), C.stride(0), _out_code(C.dtype), _stream(A.device)))
+    return C
 
 
 # --- the pages' call signatures ------------------------------------------

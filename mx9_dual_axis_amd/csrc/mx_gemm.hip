@@ -1,0 +1,251 @@
+// mx_gemm.hip -- MXFP8 block-scaled contraction on gfx950 matrix cores.
+//
+// Operation: AMD-AGI/ALTO PR #31, "Add MXFP8 grouped GEMM (E4M3) for
+// routed-expert MoE training" (description): E4M3 operands with E8M0 scales
+// per 32 elements of the contraction, groups given by 1-D cumulative
+// offsets.  Both operands are stored with the contraction index contiguous
+// ("NT"), which is what the dual-axis cast emits: q_row [M, K] for the
+// forward and q_col [K, M] (tokens contiguous) for the weight gradient.
+//
+//   C[m][n] = sum_k e4m3(A[m][k]) 2^(sA(m, k/32) - 127) e4m3(B[n][k]) 2^(sB(n, k/32) - 127)
+//
+// Matrix-core layout of v_mfma_scale_f32_16x16x128_f8f6f4 (identified on
+// MI355X with one-hot probes): lane L of a wave holds row L % 16 of the
+// 16 x 128 operand; with g = L / 16 its bytes 0..15 are k = 16g .. 16g+15
+// and bytes 16..31 are k = 64 + 16g .. 64 + 16g + 15, and its scale operand
+// is the E8M0 byte of k-block [32g, 32g + 32).  The result C[4 (L/16) + v]
+// [L % 16] is element v of lane L's four accumulators.  The same layout for
+// A and B means each lane reads two 16-byte pieces of one stored row.
+//
+// Work decomposition: one workgroup (4 wave64s) per 128 x 128 tile of C;
+// wave w computes the 64 x 64 quarter (w / 2, w % 2) as 4 x 4 instructions
+// per 128-wide step of the contraction.
+//   * staging: the A and B tiles of a step (128 rows x 128 bytes each) are
+//     loaded with 16-byte global loads (a wave covers eight whole 128-byte
+//     rows) into double-buffered LDS; the 16-byte chunk index of a row is
+//     XORed with row % 8 so that the 16 rows a fragment read touches at one
+//     chunk offset fall in different banks.  The next step's loads are in
+//     flight while the current step computes.
+//   * scales: a lane needs one A byte per 16-row sub-tile and one B byte per
+//     16-column sub-tile per step; the four A bytes (and the four B bytes)
+//     are packed into one register and the instruction's op_sel picks the
+//     byte.  They are fetched one step ahead, like the data.
+//   * groups: row groups (the forward: rows of group g use expert g's
+//     operand, rows past the last offset give 0) find their group from the
+//     tile's first row, since groups are multiples of 128 rows; contraction
+//     groups (the weight gradient) give each group its own C and run the
+//     group's range of the contraction.
+#include "mxq_kernels.h"
+
+namespace mxq {
+namespace {
+
+constexpr int kTile = 128;
+constexpr int kThreads = 256;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+struct GemmArgs {
+    const uint8_t* A;
+    int64_t lda;
+    const uint8_t* sA;
+    int64_t sa_rs, sa_bs;
+    const uint8_t* B;
+    int64_t ldb, b_gs;
+    const uint8_t* sB;
+    int64_t sb_rs, sb_bs, sb_gs;
+    void* C;
+    int64_t ldc, c_gs;
+    int64_t M, N, K;          // rows of A and C, rows of B, contraction extent
+    const int32_t* offs;
+    int32_t G;
+    int32_t mode;             // 0: dense or row groups, 1: contraction groups
+    uint32_t tiles_m, tiles_n;
+};
+
+template <int MS, int NS>
+__device__ __forceinline__ void mma(v4f (&acc)[4][4], const v8i (&a)[4], const v8i (&b)[4], int sa, int sb) {
+    acc[MS][NS] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[MS], b[NS], acc[MS][NS], 0, 0, MS, sa, NS, sb);
+}
+
+template <int MS>
+__device__ __forceinline__ void mma_row(v4f (&acc)[4][4], const v8i (&a)[4], const v8i (&b)[4], int sa, int sb) {
+    mma<MS, 0>(acc, a, b, sa, sb);
+    mma<MS, 1>(acc, a, b, sa, sb);
+    mma<MS, 2>(acc, a, b, sa, sb);
+    mma<MS, 3>(acc, a, b, sa, sb);
+}
+
+// Clamp a group end to [lo, hi] and down to a multiple of the tile, so that
+// invalid offsets can never move an access outside the operands.
+__device__ __forceinline__ int64_t clamp_end(int64_t v, int64_t lo, int64_t hi) {
+    v = v < lo ? lo : (v > hi ? hi : v);
+    return v - (v - lo) % kTile;
+}
+
+template <int kOut>
+__global__ __launch_bounds__(kThreads, 2)
+void mx_gemm_kernel(GemmArgs p) {
+    __shared__ uint4 lds[2][2][kTile * 8];      // [buffer][A, B][row * 8 + chunk]
+
+    const uint32_t t = threadIdx.x;
+    const uint32_t lane = t & 63u, wave = t >> 6;
+    const uint32_t wm = wave >> 1, wn = wave & 1u;
+
+    // ---- which tile, which group, which range of the contraction ----
+    uint32_t tm, tn;
+    int64_t k_lo = 0, k_hi = p.K;
+    const uint8_t* B = p.B;
+    const uint8_t* sB = p.sB;
+    char* C = static_cast<char*>(p.C);
+    bool zero = false;
+    if (p.mode == 0) {
+        tm = blockIdx.x % p.tiles_m;
+        tn = blockIdx.x / p.tiles_m;
+        if (p.offs != nullptr) {
+            const int64_t row = int64_t(tm) * kTile;
+            int32_t g = 0;
+            while (g < p.G && int64_t(p.offs[g]) <= row) ++g;      // first group ending after the row
+            if (g == p.G) {
+                zero = true;                                        // the uncovered tail
+            } else {
+                B += int64_t(g) * p.b_gs;
+                sB += int64_t(g) * p.sb_gs;
+            }
+        }
+    } else {
+        const uint32_t per = p.tiles_m * p.tiles_n;
+        const uint32_t g = blockIdx.x / per, r = blockIdx.x - g * per;
+        tm = r % p.tiles_m;
+        tn = r / p.tiles_m;
+        k_lo = g == 0 ? 0 : clamp_end(p.offs[g - 1], 0, p.K);
+        k_hi = clamp_end(p.offs[g], k_lo, p.K);
+        C += int64_t(g) * p.c_gs * (kOut == 0 ? 4 : 2);
+    }
+    const int64_t m0 = int64_t(tm) * kTile, n0 = int64_t(tn) * kTile;
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    if (!zero && k_lo < k_hi) {
+        uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+        // scale rows of this lane's four A sub-tiles and four B sub-tiles
+        const uint8_t* sa_row = p.sA + (m0 + wm * 64 + (lane & 15u)) * p.sa_rs;
+        const uint8_t* sb_row = sB + (n0 + wn * 64 + (lane & 15u)) * p.sb_rs;
+        const int64_t kgrp = int64_t(lane >> 4);                   // the lane's 32-wide k-block of a step
+        // this thread's four staging chunks: c = t + 256 i, row c / 8, 16-byte piece c % 8
+        const uint32_t r0 = t >> 3, ch = t & 7u;                    // rows r0, r0 + 32, r0 + 64, r0 + 96
+        const uint8_t* ga = p.A + (m0 + r0) * p.lda + 16 * ch;
+        const uint8_t* gb = B + (n0 + r0) * p.ldb + 16 * ch;
+        const int64_t lda32 = 32 * p.lda, ldb32 = 32 * p.ldb;
+        const uint32_t slot0 = r0 * 8u + (ch ^ (r0 & 7u));         // (r0 + 32 i) % 8 == r0 % 8
+#define MXQ_LOAD_STEP(k, SA, SB)                                                              \
+        do {                                                                                  \
+            ra0 = *reinterpret_cast<const uint4*>(ga + (k));                                  \
+            ra1 = *reinterpret_cast<const uint4*>(ga + lda32 + (k));                          \
+            ra2 = *reinterpret_cast<const uint4*>(ga + 2 * lda32 + (k));                      \
+            ra3 = *reinterpret_cast<const uint4*>(ga + 3 * lda32 + (k));                      \
+            rb0 = *reinterpret_cast<const uint4*>(gb + (k));                                  \
+            rb1 = *reinterpret_cast<const uint4*>(gb + ldb32 + (k));                          \
+            rb2 = *reinterpret_cast<const uint4*>(gb + 2 * ldb32 + (k));                      \
+            rb3 = *reinterpret_cast<const uint4*>(gb + 3 * ldb32 + (k));                      \
+            const int64_t blk_ = (k) / 32 + kgrp;                                             \
+            uint32_t a4_ = 0, b4_ = 0;                                                        \
+            for (int s_ = 0; s_ < 4; ++s_) {                                                  \
+                a4_ |= uint32_t(sa_row[16 * s_ * p.sa_rs + blk_ * p.sa_bs]) << (8 * s_);      \
+                b4_ |= uint32_t(sb_row[16 * s_ * p.sb_rs + blk_ * p.sb_bs]) << (8 * s_);      \
+            }                                                                                 \
+            SA = int(a4_);                                                                    \
+            SB = int(b4_);                                                                    \
+        } while (0)
+#define MXQ_STORE_STEP(buf)                                                                   \
+        do {                                                                                  \
+            lds[buf][0][slot0] = ra0;                                                         \
+            lds[buf][0][slot0 + 256] = ra1;                                                   \
+            lds[buf][0][slot0 + 512] = ra2;                                                   \
+            lds[buf][0][slot0 + 768] = ra3;                                                   \
+            lds[buf][1][slot0] = rb0;                                                         \
+            lds[buf][1][slot0 + 256] = rb1;                                                   \
+            lds[buf][1][slot0 + 512] = rb2;                                                   \
+            lds[buf][1][slot0 + 768] = rb3;                                                   \
+        } while (0)
+
+        int sa_cur, sb_cur, sa_nxt = 0, sb_nxt = 0;
+        MXQ_LOAD_STEP(k_lo, sa_cur, sb_cur);
+        MXQ_STORE_STEP(0);
+        __syncthreads();
+        int buf = 0;
+        for (int64_t k = k_lo; k < k_hi; k += kTile) {
+            const bool more = k + kTile < k_hi;
+            if (more) MXQ_LOAD_STEP(k + kTile, sa_nxt, sb_nxt);
+            v8i af[4], bf[4];
+            const uint32_t g = lane >> 4;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint32_t ar = wm * 64 + 16 * s + (lane & 15u);
+                const uint4 alo = lds[buf][0][ar * 8u + (g ^ (ar & 7u))];
+                const uint4 ahi = lds[buf][0][ar * 8u + ((4u + g) ^ (ar & 7u))];
+                af[s] = v8i{int(alo.x), int(alo.y), int(alo.z), int(alo.w), int(ahi.x), int(ahi.y), int(ahi.z), int(ahi.w)};
+                const uint32_t br = wn * 64 + 16 * s + (lane & 15u);
+                const uint4 blo = lds[buf][1][br * 8u + (g ^ (br & 7u))];
+                const uint4 bhi = lds[buf][1][br * 8u + ((4u + g) ^ (br & 7u))];
+                bf[s] = v8i{int(blo.x), int(blo.y), int(blo.z), int(blo.w), int(bhi.x), int(bhi.y), int(bhi.z), int(bhi.w)};
+            }
+            mma_row<0>(acc, af, bf, sa_cur, sb_cur);
+            mma_row<1>(acc, af, bf, sa_cur, sb_cur);
+            mma_row<2>(acc, af, bf, sa_cur, sb_cur);
+            mma_row<3>(acc, af, bf, sa_cur, sb_cur);
+            if (more) {
+                MXQ_STORE_STEP(buf ^ 1);
+                sa_cur = sa_nxt;
+                sb_cur = sb_nxt;
+            }
+            __syncthreads();
+            buf ^= 1;
+        }
+#undef MXQ_LOAD_STEP
+#undef MXQ_STORE_STEP
+    }
+
+    // ---- epilogue: C[m0 + 64 wm + 16 ms + 4 (lane / 16) + v][n0 + 64 wn + 16 ns + lane % 16] ----
+    const int64_t col0 = n0 + wn * 64 + (lane & 15u);
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t row = m0 + wm * 64 + 16 * ms + 4 * (lane >> 4) + v;
+#pragma unroll
+            for (int ns = 0; ns < 4; ++ns) {
+                const float x = acc[ms][ns][v];
+                const int64_t idx = row * p.ldc + col0 + 16 * ns;
+                if (kOut == 0) reinterpret_cast<float*>(C)[idx] = x;
+                else reinterpret_cast<__bf16*>(C)[idx] = __bf16(x);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_mx_gemm(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, int64_t sa_bs,
+                          const uint8_t* B, int64_t ldb, int64_t b_gs, const uint8_t* sB, int64_t sb_rs,
+                          int64_t sb_bs, int64_t sb_gs, void* C, int64_t ldc, int64_t c_gs, int64_t M, int64_t N,
+                          int64_t K, const int32_t* offs, int32_t G, int mode, int out_dtype, hipStream_t stream) {
+    GemmArgs p;
+    p.A = A; p.lda = lda; p.sA = sA; p.sa_rs = sa_rs; p.sa_bs = sa_bs;
+    p.B = B; p.ldb = ldb; p.b_gs = b_gs; p.sB = sB; p.sb_rs = sb_rs; p.sb_bs = sb_bs; p.sb_gs = sb_gs;
+    p.C = C; p.ldc = ldc; p.c_gs = c_gs;
+    p.M = M; p.N = N; p.K = K; p.offs = offs; p.G = G; p.mode = mode;
+    p.tiles_m = uint32_t(M / kTile);
+    p.tiles_n = uint32_t(N / kTile);
+    const uint32_t tiles = p.tiles_m * p.tiles_n * uint32_t(mode == 1 ? G : 1);
+    if (out_dtype == 0) hipLaunchKernelGGL(mx_gemm_kernel<0>, dim3(tiles), dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL(mx_gemm_kernel<1>, dim3(tiles), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace mxq

@@ -75,6 +75,33 @@ int check_mx9_view(int32_t dtype, int64_t outer, int64_t len, int64_t inner, int
     return MX_OK;
 }
 
+// Bytes spanned by a strided scale view of rows x blocks (non-negative strides).
+uint64_t scale_span(int64_t rows, int64_t blocks, int64_t rs, int64_t bs) {
+    if (rows <= 0 || blocks <= 0) return 0;
+    return uint64_t((rows - 1) * rs + (blocks - 1) * bs + 1);
+}
+
+constexpr int64_t kMaxGemm = int64_t(1) << 24;
+
+// Checks shared by the contraction calls: operand pitches and alignment,
+// scale strides, the output type and pitch.  K is the contraction extent.
+int check_gemm(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, int64_t sa_bs,
+               const uint8_t* B, int64_t ldb, const uint8_t* sB, int64_t sb_rs, int64_t sb_bs,
+               int64_t M, int64_t N, int64_t K, const void* C, int64_t ldc, int32_t out_dtype) {
+    const bool empty = M == 0 || N == 0;
+    if (!empty && (!A || !sA || !B || !sB || !C)) return MX_E_NULL;
+    if (out_dtype != MX_DTYPE_F32 && out_dtype != MX_DTYPE_BF16) return MX_E_DTYPE;
+    if (M < 0 || N < 0 || K < 0 || M > kMaxGemm || N > kMaxGemm || K > kMaxGemm ||
+        M % 128 != 0 || N % 128 != 0 || K % 128 != 0)
+        return MX_E_SHAPE;
+    if (lda < K || ldb < K || lda % 16 != 0 || ldb % 16 != 0 || lda > kMaxGemm || ldb > kMaxGemm || ldc < N ||
+        ldc > kMaxGemm || sa_rs < 0 || sa_bs < 0 || sb_rs < 0 || sb_bs < 0)
+        return MX_E_STRIDE;
+    const uintptr_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
+    if (!empty && (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, esz))) return MX_E_ALIGN;
+    return MX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -255,6 +282,73 @@ int mx9_unpack_records(const uint8_t* packed, int64_t ld_p, int64_t outer, int64
     if (nb == 0) return MX_OK;
     hipError_t e = mxq::launch_mx9_unpack_records(packed, ld_p, outer, len, inner, out_dtype, y,
                                                   static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+}
+
+int mx_gemm_nt(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, int64_t sa_bs,
+               const uint8_t* B, int64_t ldb, const uint8_t* sB, int64_t sb_rs, int64_t sb_bs,
+               int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, int32_t out_dtype, void* stream) {
+    int rc = check_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, sB, sb_rs, sb_bs, M, N, K, C, ldc, out_dtype);
+    if (rc != MX_OK) return rc;
+    const uint64_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
+    const uint64_t cb = matrix_bytes(M, N, ldc, int64_t(esz));
+    const Span s[5] = {{addr(C), cb}, {addr(A), matrix_bytes(M, K, lda, 1)}, {addr(B), matrix_bytes(N, K, ldb, 1)},
+                       {addr(sA), scale_span(M, K / 32, sa_rs, sa_bs)}, {addr(sB), scale_span(N, K / 32, sb_rs, sb_bs)}};
+    for (int i = 1; i < 5; ++i)
+        if (overlap(s[0], s[i])) return MX_E_OVERLAP;
+    if (M == 0 || N == 0) return MX_OK;
+    hipError_t e = mxq::launch_mx_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, 0, sB, sb_rs, sb_bs, 0, C, ldc, 0, M, N, K,
+                                       nullptr, 1, 0, out_dtype, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+}
+
+int mx_grouped_gemm_rows(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, int64_t sa_bs,
+                         const uint8_t* B, int64_t ldb, int64_t b_gs, const uint8_t* sB, int64_t sb_rs,
+                         int64_t sb_bs, int64_t sb_gs, const int32_t* offs, int32_t G, int64_t M, int64_t N,
+                         int64_t K, void* C, int64_t ldc, int32_t out_dtype, void* stream) {
+    int rc = check_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, sB, sb_rs, sb_bs, M, N, K, C, ldc, out_dtype);
+    if (rc != MX_OK) return rc;
+    if (G < 1 || G > (1 << 20)) return MX_E_SHAPE;
+    if (!offs) return MX_E_NULL;
+    if (!aligned(offs, 4)) return MX_E_ALIGN;
+    if (b_gs < 0 || sb_gs < 0) return MX_E_STRIDE;
+    const uint64_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
+    const Span s[6] = {{addr(C), matrix_bytes(M, N, ldc, int64_t(esz))}, {addr(A), matrix_bytes(M, K, lda, 1)},
+                       {addr(B), uint64_t(G - 1) * uint64_t(b_gs) + matrix_bytes(N, K, ldb, 1)},
+                       {addr(sA), scale_span(M, K / 32, sa_rs, sa_bs)},
+                       {addr(sB), uint64_t(G - 1) * uint64_t(sb_gs) + scale_span(N, K / 32, sb_rs, sb_bs)},
+                       {addr(offs), uint64_t(G) * 4}};
+    for (int i = 1; i < 6; ++i)
+        if (overlap(s[0], s[i])) return MX_E_OVERLAP;
+    if (M == 0 || N == 0) return MX_OK;
+    hipError_t e = mxq::launch_mx_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, b_gs, sB, sb_rs, sb_bs, sb_gs, C, ldc, 0,
+                                       M, N, K, offs, G, 0, out_dtype, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+}
+
+int mx_grouped_gemm_k(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, int64_t sa_bs,
+                      const uint8_t* B, int64_t ldb, const uint8_t* sB, int64_t sb_rs, int64_t sb_bs,
+                      const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* C, int64_t ldc,
+                      int64_t c_gs, int32_t out_dtype, void* stream) {
+    int rc = check_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, sB, sb_rs, sb_bs, M, N, K, C, ldc, out_dtype);
+    if (rc != MX_OK) return rc;
+    if (G < 1 || G > (1 << 20)) return MX_E_SHAPE;
+    if (!offs) return MX_E_NULL;
+    if (!aligned(offs, 4)) return MX_E_ALIGN;
+    const uint64_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
+    const uint64_t slab = matrix_bytes(M, N, ldc, 1);                  // elements of one group's C
+    if (c_gs < int64_t(slab)) return MX_E_STRIDE;
+    const uint64_t tiles = uint64_t(M / 128) * uint64_t(N / 128) * uint64_t(G);
+    if (tiles > 0x7FFFFFFFull) return MX_E_SHAPE;
+    const Span s[6] = {{addr(C), (uint64_t(G - 1) * uint64_t(c_gs) + slab) * esz},
+                       {addr(A), matrix_bytes(M, K, lda, 1)}, {addr(B), matrix_bytes(N, K, ldb, 1)},
+                       {addr(sA), scale_span(M, K / 32, sa_rs, sa_bs)}, {addr(sB), scale_span(N, K / 32, sb_rs, sb_bs)},
+                       {addr(offs), uint64_t(G) * 4}};
+    for (int i = 1; i < 6; ++i)
+        if (overlap(s[0], s[i])) return MX_E_OVERLAP;
+    if (M == 0 || N == 0) return MX_OK;
+    hipError_t e = mxq::launch_mx_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, 0, sB, sb_rs, sb_bs, 0, C, ldc, c_gs, M, N,
+                                       K, offs, G, 1, out_dtype, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
 }
 

@@ -45,4 +45,14 @@ hipError_t launch_mx9_pack_records(const void* x, int dtype, int64_t outer, int6
 hipError_t launch_mx9_unpack_records(const uint8_t* packed, int64_t ld_p, int64_t outer, int64_t len,
                                      int64_t inner, int out_dtype, void* y, hipStream_t stream);
 
+// MXFP8 block-scaled contraction C = A B^T (codes with the contraction
+// contiguous, E8M0 scales per 32 through strided views).  mode 0: dense
+// (offs == nullptr) or row groups (group g's rows use B + g * b_gs, rows past
+// offs[G-1] give 0); mode 1: contraction groups (group g writes C + g * c_gs
+// from its contraction range).  M, N, K are multiples of 128.
+hipError_t launch_mx_gemm(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, int64_t sa_bs,
+                          const uint8_t* B, int64_t ldb, int64_t b_gs, const uint8_t* sB, int64_t sb_rs,
+                          int64_t sb_bs, int64_t sb_gs, void* C, int64_t ldc, int64_t c_gs, int64_t M, int64_t N,
+                          int64_t K, const int32_t* offs, int32_t G, int mode, int out_dtype, hipStream_t stream);
+
 }  // namespace mxq

@@ -25,7 +25,7 @@ def _declared():
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["mx_quantize_2d_dual", "mx_quantize_grouped", "mx9_pack", "mx9_unpack",
                                   "mx9_pack_axis", "mx9_unpack_axis", "mx9_pack_records", "mx9_unpack_records",
-                                  "mx_status_string"])
+                                  "mx_gemm_nt", "mx_grouped_gemm_rows", "mx_grouped_gemm_k", "mx_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -133,6 +133,37 @@ def test_mx9_axis_and_record_validation_codes():
     assert unpack_rec(pk=None) == 1 and unpack_rec(od=2) == 2 and unpack_rec(ld=10) == 6
     assert unpack_rec(y=FAKE * 5 + 2) == 7 and unpack_rec(y=FAKE * 2 + 100) == 8
     assert unpack_rec(inner=0, y=None, pk=None) == 0
+
+
+def test_gemm_validation_codes():
+    lib = mxq.library()
+
+    def gemm(A=FAKE, lda=256, sA=FAKE * 2, rs=8, bs=1, B=FAKE * 3, ldb=256, sB=FAKE * 4, M=128, N=128, K=256,
+             C=FAKE * 5, ldc=128, od=0):
+        return lib.mx_gemm_nt(A, lda, sA, rs, bs, B, ldb, sB, 8, 1, M, N, K, C, ldc, od, None)
+    assert gemm(A=None) == 1 and gemm(C=None) == 1 and gemm(od=2) == 2
+    assert gemm(M=100) == 5 and gemm(K=96) == 5 and gemm(N=-128) == 5 and gemm(M=1 << 25) == 5
+    assert gemm(lda=128) == 6 and gemm(lda=264) == 6 and gemm(ldc=64) == 6 and gemm(rs=-1) == 6
+    assert gemm(A=FAKE + 8) == 7 and gemm(C=FAKE * 5 + 2) == 7
+    assert gemm(C=FAKE + 1024) == 8                                  # C inside A
+    assert gemm(sA=FAKE * 5 + 64) == 8                               # scales inside C
+    assert gemm(M=0, A=None, sA=None, B=None, sB=None, C=None) == 0
+
+    def rows(G=4, offs=FAKE * 6, bgs=1 << 16, **kw):
+        a = dict(A=FAKE, sA=FAKE * 2, B=FAKE * 3, sB=FAKE * 4, C=FAKE * 5)
+        a.update(kw)
+        return lib.mx_grouped_gemm_rows(a["A"], 256, a["sA"], 8, 1, a["B"], 256, bgs, a["sB"], 8, 1, 1024, offs, G,
+                                        128, 128, 256, a["C"], 128, 0, None)
+    assert rows(G=0) == 5 and rows(offs=None) == 1 and rows(offs=FAKE * 6 + 2) == 7 and rows(bgs=-1) == 6
+    assert rows(C=FAKE * 3 + 3 * (1 << 16)) == 8                     # C inside expert 3's operand
+
+    def kgroups(G=4, cgs=128 * 128, **kw):
+        a = dict(A=FAKE, sA=FAKE * 2, B=FAKE * 3, sB=FAKE * 4, C=FAKE * 5)
+        a.update(kw)
+        return lib.mx_grouped_gemm_k(a["A"], 256, a["sA"], 8, 1, a["B"], 256, a["sB"], 8, 1, FAKE * 6, G,
+                                     128, 128, 256, a["C"], 128, cgs, 0, None)
+    assert kgroups(G=0) == 5 and kgroups(cgs=128 * 127) == 6
+    assert kgroups(C=FAKE * 6 - 4 * 128 * 128 * 2) == 8              # the last group's C runs into offs
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch):

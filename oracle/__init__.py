@@ -422,3 +422,40 @@ def mx_grouped_gemm_k(A, sA, B, sB, offs, *, sa_strides, sb_strides, threads: in
                                        k0=int(lo), k1=int(hi), threads=threads, with_abs=True)
         lo = hi
     return (C, absC) if with_abs else C
+
+
+# ---------------------------------------------------------------------------
+# Matrix-core scale layout (a layout of this build for the MXFP8 contraction's
+# consumer; the pages ask for scales in the consumer's own layout so that no
+# rearrangement runs between the cast and the GEMM)
+# ---------------------------------------------------------------------------
+
+def mfma_scale_index(r, b, kb: int):
+    """Byte position of scale S[r][b] (row r of the operand, 32-wide block b of
+    its contraction, kb blocks per row) in the matrix-core layout: for each
+    64-row group and each 4-block (128-wide) step, 64 dwords, one per lane L of
+    the 16x16x128 instruction, lane L = 16 (b % 4) + r % 16 holding in byte
+    (r % 64) // 16 the scale of its sub-tile (r // 16) % 4."""
+    r = np.asarray(r, dtype=np.int64)
+    b = np.asarray(b, dtype=np.int64)
+    return ((((r // 64) * (kb // 4) + b // 4) * 64 + (b % 4) * 16 + r % 16) * 4 + (r % 64) // 16)
+
+
+def scales_to_mfma(S):
+    """Plain scales S [R, kb] (R a multiple of 64, kb of 4) -> the same bytes
+    in the matrix-core layout, as a flat uint8 array of R * kb bytes."""
+    S = np.asarray(S, dtype=np.uint8)
+    R, kb = S.shape
+    if R % 64 or kb % 4:
+        raise ValueError("rows must be a multiple of 64 and blocks a multiple of 4")
+    out = np.empty(R * kb, np.uint8)
+    r, b = np.meshgrid(np.arange(R), np.arange(kb), indexing="ij")
+    out[mfma_scale_index(r, b, kb)] = S
+    return out
+
+
+def scales_from_mfma(flat, R: int, kb: int):
+    """Inverse of scales_to_mfma."""
+    flat = np.asarray(flat, dtype=np.uint8).reshape(-1)
+    r, b = np.meshgrid(np.arange(R), np.arange(kb), indexing="ij")
+    return flat[mfma_scale_index(r, b, kb)]

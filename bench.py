@@ -192,23 +192,31 @@ def measure_configs(dev, launches: int, sets: int = 3):
     u8 = dict(dtype=torch.uint8, device=dev)
     res = {}
 
-    def dual_sets(xb, offs=None):
+    def dual_sets(xb, offs=None, layout="plain"):
         Mc, Nc = xb.shape
         x0 = dev_bf16(xb)
         xs = [x0] + [x0.clone() for _ in range(sets - 1)]
         outs = [(torch.empty((Mc, Nc), **u8), torch.empty((Mc, Nc // 32), **u8),
                  torch.empty((Nc, Mc), **u8), torch.empty((Mc // 32, Nc), **u8)) for _ in range(sets)]
+        if layout == "mfma":
+            outs = [(q, sr.view(-1), qc, sc.view(-1)) for q, sr, qc, sc in outs]
         if offs is None:
-            return [lambda x=x, o=o: mxq.mx_quantize_2d_dual(x, out=o) for x, o in zip(xs, outs)]
+            return [lambda x=x, o=o: mxq.mx_quantize_2d_dual(x, out=o, scale_layout=layout) for x, o in zip(xs, outs)]
         od = torch.from_numpy(offs).to(dev)
         err = torch.zeros(1, dtype=torch.int32, device=dev)
-        return [lambda x=x, o=o: mxq.mx_quantize_grouped(x, od, err=err, out=o) for x, o in zip(xs, outs)]
+        return [lambda x=x, o=o: mxq.mx_quantize_grouped(x, od, err=err, out=o, scale_layout=layout)
+                for x, o in zip(xs, outs)]
 
     print("bench: dense cast, mixed bf16 [8192, 7168]", file=sys.stderr, flush=True)
     xb = synth.dual_mixed()
     calls = dual_sets(xb)
     res["dual_mixed"] = dict(workload="dense dual-axis cast, mixed-magnitude bf16 [8192, 7168]",
                              **summarize(time_rotating(calls, launches), xb.size * DUAL_BYTES_PER_ELEM))
+    del calls
+    calls = dual_sets(xb, layout="mfma")
+    res["dual_mixed_mfma"] = dict(workload="dense dual-axis cast, mixed-magnitude bf16 [8192, 7168], scales in "
+                                           "the matrix-core layout",
+                                  **summarize(time_rotating(calls, launches), xb.size * DUAL_BYTES_PER_ELEM))
     del calls
 
     print("bench: grouped cast, bf16 [16384, 5120], 64 groups", file=sys.stderr, flush=True)
@@ -217,6 +225,11 @@ def measure_configs(dev, launches: int, sets: int = 3):
     res["grouped"] = dict(workload="grouped dual-axis cast, bf16 [16384, 5120], 64 groups, offs[-1] = "
                                    f"{int(offs[-1])}",
                           **summarize(time_rotating(calls, launches), xb.size * DUAL_BYTES_PER_ELEM + 4 * offs.size))
+    del calls
+    calls = dual_sets(xb, offs, layout="mfma")
+    res["grouped_mfma"] = dict(workload="grouped dual-axis cast, bf16 [16384, 5120], 64 groups, scales in the "
+                                        "matrix-core layout",
+                               **summarize(time_rotating(calls, launches), xb.size * DUAL_BYTES_PER_ELEM + 4 * offs.size))
     del calls
 
     print("bench: MX9 pack/unpack, weights [4096, 14336] fp32 and bf16", file=sys.stderr, flush=True)
@@ -293,6 +306,7 @@ def measure_gemm(dev, launches: int):
     x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
     od = torch.from_numpy(offs).to(dev)
     q_row, s_row, q_col, s_col = mxq.mx_quantize_grouped(x, od)
+    m_row, ms_row, m_col, ms_col = mxq.mx_quantize_grouped(x, od, scale_layout="mfma")
     del x
 
     def codes(shape):
@@ -310,7 +324,11 @@ def measure_gemm(dev, launches: int):
     res["gemm_grouped_forward"] = tsum(time_rotating(fwd, launches), 2.0 * covered * N * K,
                                        f"grouped forward, cast activations [{Mt}, {K}] (64 groups, {covered} rows) "
                                        f"x 64 experts [{N}, {K}] -> bf16")
-    del W, sW, out, fwd
+    sWm = sW.reshape(E, N * K // 32)       # random bytes: read as the matrix-core layout
+    fwd = [lambda: mxq.mx_grouped_gemm_rows_mfma(m_row, ms_row, W, sWm, od, out=out)]
+    res["gemm_grouped_forward_mfma"] = tsum(time_rotating(fwd, launches), 2.0 * covered * N * K,
+                                            "grouped forward as above, scales in the matrix-core layout")
+    del W, sW, sWm, out, fwd
     dY = codes((N, Mt))
     sdY = scales((Mt // 32, N))
     dW = torch.empty((E, K, N), dtype=torch.bfloat16, device=dev)
@@ -318,14 +336,22 @@ def measure_gemm(dev, launches: int):
     res["gemm_grouped_wgrad"] = tsum(time_rotating(wg, launches), 2.0 * covered * N * K,
                                      f"grouped weight gradient, cast q_col [{K}, {Mt}] x dY [{N}, {Mt}] over 64 groups "
                                      f"-> bf16 [64, {K}, {N}]")
-    del dY, sdY, dW, wg, q_row, s_row, q_col, s_col
+    sdYm = sdY.reshape(-1)
+    wg = [lambda: mxq.mx_grouped_gemm_k_mfma(m_col, ms_col, dY, sdYm, od, out=dW)]
+    res["gemm_grouped_wgrad_mfma"] = tsum(time_rotating(wg, launches), 2.0 * covered * N * K,
+                                          "grouped weight gradient as above, scales in the matrix-core layout")
+    del dY, sdY, sdYm, dW, wg, q_row, s_row, q_col, s_col, m_row, ms_row, m_col, ms_col
     D = 8192
     A, B = codes((D, D)), codes((D, D))
     sA, sB = scales((D, D // 32)), scales((D, D // 32))
     C = torch.empty((D, D), dtype=torch.bfloat16, device=dev)
     dn = [lambda: mxq.mx_gemm_nt(A, sA, B, sB, out=C)]
     res["gemm_dense_8192"] = tsum(time_rotating(dn, launches), 2.0 * D ** 3, "dense [8192, 8192, 8192] -> bf16")
-    del A, B, sA, sB, C, dn
+    sAm, sBm = sA.reshape(-1), sB.reshape(-1)
+    dn = [lambda: mxq.mx_gemm_nt_mfma(A, sAm, B, sBm, out=C)]
+    res["gemm_dense_8192_mfma"] = tsum(time_rotating(dn, launches), 2.0 * D ** 3,
+                                       "dense [8192, 8192, 8192] -> bf16, scales in the matrix-core layout")
+    del A, B, sA, sB, sAm, sBm, C, dn
     torch.cuda.synchronize()
     return res
 

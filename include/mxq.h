@@ -116,6 +116,49 @@ int mx_quantize_grouped(const uint16_t *x, int64_t M, int64_t N, int64_t ld_x,
                         int32_t *err, void *stream);
 
 /*
+ * Matrix-core scale layout.  The _mfma variants below write (casts) or read
+ * (contractions) E8M0 scales in the order in which the gfx950 scaled matrix
+ * instruction (16x16x128, E4M3 operands) takes them, so that a consumer
+ * loads one dword per lane per 128-wide step and no rearrangement runs
+ * between the cast and the contraction ([MXFP8], PR description: the kernel
+ * emits the consumer's swizzled scale layout directly).  For an operand of R
+ * rows (R a multiple of 64) and K/32 blocks per row (K a multiple of 128),
+ * scale (r, b) is the byte
+ *
+ *     ((r/64 * K/128 + b/4) * 64 + 16 * (b%4) + r%16) * 4 + (r%64)/16
+ *
+ * of an R * K/32 byte buffer: each 64-row group and 4-block step owns 256
+ * contiguous bytes, dword L of which holds, in byte q, the scale of row
+ * 64 (r/64) + 16 q + L%16 for block 4 (b/4) + L/16.
+ */
+
+/*
+ * mx_quantize_2d_dual_mfma -- mx_quantize_2d_dual with both scale tensors in
+ * the matrix-core layout: s_row as the operand [M rows, N/32 blocks] (the
+ * scales of q_row), s_col as the operand [N rows, M/32 blocks] (the scales
+ * of q_col, whose rows are the input's columns).  Byte for byte the same
+ * scale values as mx_quantize_2d_dual, permuted; q_row and q_col identical.
+ * Arguments and errors as for mx_quantize_2d_dual.  One kernel.
+ */
+int mx_quantize_2d_dual_mfma(const uint16_t *x, int64_t M, int64_t N, int64_t ld_x,
+                             int32_t block_size, int32_t scaling_mode,
+                             uint8_t *q_row, uint8_t *s_row,
+                             uint8_t *q_col, uint8_t *s_col, void *stream);
+
+/*
+ * mx_quantize_grouped_mfma -- mx_quantize_grouped with the scales of
+ * mx_quantize_2d_dual_mfma; the zeroed tail is the same set of s_col bytes
+ * (blocks b >= offs[G-1]/32 of every row of the [N, M/32] operand).
+ * Arguments and errors as for mx_quantize_grouped.
+ */
+int mx_quantize_grouped_mfma(const uint16_t *x, int64_t M, int64_t N, int64_t ld_x,
+                             int32_t block_size, int32_t scaling_mode,
+                             const int32_t *offs, int32_t G,
+                             uint8_t *q_row, uint8_t *s_row,
+                             uint8_t *q_col, uint8_t *s_col,
+                             int32_t *err, void *stream);
+
+/*
  * mx9_pack -- MX9 pack along the last axis, block 16 ([MX9], Summary and
  * Key design choices).
  *
@@ -288,6 +331,26 @@ int mx_grouped_gemm_k(const uint8_t *A, int64_t lda, const uint8_t *sA, int64_t 
                       const uint8_t *B, int64_t ldb, const uint8_t *sB, int64_t sb_rs, int64_t sb_bs,
                       const int32_t *offs, int32_t G, int64_t M, int64_t N, int64_t K, void *C, int64_t ldc,
                       int64_t c_gs, int32_t out_dtype, void *stream);
+
+/*
+ * mx_gemm_nt_mfma, mx_grouped_gemm_rows_mfma, mx_grouped_gemm_k_mfma -- the
+ * three contractions above with sA, sB in the matrix-core scale layout (sA
+ * for the operand [M rows, K/32 blocks], sB for [N rows, K/32 blocks]; for
+ * the row-grouped form expert g's scales start at sB + g * sb_gs), which the
+ * _mfma casts emit: s_row for q_row, s_col for q_col.  The scale pointers
+ * must be 16-byte aligned (MX_E_ALIGN).  Results, other arguments and
+ * errors as for the strided-view forms.
+ */
+int mx_gemm_nt_mfma(const uint8_t *A, int64_t lda, const uint8_t *sA, const uint8_t *B, int64_t ldb,
+                    const uint8_t *sB, int64_t M, int64_t N, int64_t K, void *C, int64_t ldc,
+                    int32_t out_dtype, void *stream);
+int mx_grouped_gemm_rows_mfma(const uint8_t *A, int64_t lda, const uint8_t *sA, const uint8_t *B, int64_t ldb,
+                              int64_t b_gs, const uint8_t *sB, int64_t sb_gs, const int32_t *offs, int32_t G,
+                              int64_t M, int64_t N, int64_t K, void *C, int64_t ldc, int32_t out_dtype,
+                              void *stream);
+int mx_grouped_gemm_k_mfma(const uint8_t *A, int64_t lda, const uint8_t *sA, const uint8_t *B, int64_t ldb,
+                           const uint8_t *sB, const int32_t *offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                           void *C, int64_t ldc, int64_t c_gs, int32_t out_dtype, void *stream);
 
 /* Host function: a static, human-readable name for an mx_status value. */
 const char *mx_status_string(int status);

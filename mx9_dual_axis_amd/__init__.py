@@ -57,6 +57,8 @@ def _load():
     P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.mx_quantize_2d_dual.argtypes = [P, I64, I64, I64, I32, I32, P, P, P, P, P]
     lib.mx_quantize_grouped.argtypes = [P, I64, I64, I64, I32, I32, P, I32, P, P, P, P, P, P]
+    lib.mx_quantize_2d_dual_mfma.argtypes = lib.mx_quantize_2d_dual.argtypes
+    lib.mx_quantize_grouped_mfma.argtypes = lib.mx_quantize_grouped.argtypes
     lib.mx9_pack.argtypes = [P, I32, I64, I64, I64, I32, P, P, P, P]
     lib.mx9_unpack.argtypes = [P, P, P, I64, I64, I32, I32, P, I64, P]
     lib.mx9_pack_axis.argtypes = [P, I32, I64, I64, I64, I32, P, P, P, P]
@@ -68,9 +70,14 @@ def _load():
                                          P, I64, I32, P]
     lib.mx_grouped_gemm_k.argtypes = [P, I64, P, I64, I64, P, I64, P, I64, I64, P, I32, I64, I64, I64, P, I64, I64,
                                       I32, P]
+    lib.mx_gemm_nt_mfma.argtypes = [P, I64, P, P, I64, P, I64, I64, I64, P, I64, I32, P]
+    lib.mx_grouped_gemm_rows_mfma.argtypes = [P, I64, P, P, I64, I64, P, I64, P, I32, I64, I64, I64, P, I64, I32, P]
+    lib.mx_grouped_gemm_k_mfma.argtypes = [P, I64, P, P, I64, P, P, I32, I64, I64, I64, P, I64, I64, I32, P]
     for f in (lib.mx_quantize_2d_dual, lib.mx_quantize_grouped, lib.mx9_pack, lib.mx9_unpack,
               lib.mx9_pack_axis, lib.mx9_unpack_axis, lib.mx9_pack_records, lib.mx9_unpack_records,
-              lib.mx_gemm_nt, lib.mx_grouped_gemm_rows, lib.mx_grouped_gemm_k):
+              lib.mx_gemm_nt, lib.mx_grouped_gemm_rows, lib.mx_grouped_gemm_k,
+              lib.mx_quantize_2d_dual_mfma, lib.mx_quantize_grouped_mfma, lib.mx_gemm_nt_mfma,
+              lib.mx_grouped_gemm_rows_mfma, lib.mx_grouped_gemm_k_mfma):
         f.restype = ctypes.c_int
     lib.mx_status_string.argtypes = [ctypes.c_int]
     lib.mx_status_string.restype = ctypes.c_char_p
@@ -111,13 +118,22 @@ def _scaling(mode) -> int:
     return -1  # rejected by the library with MX_E_MODE
 
 
-def _dual_outputs(x: torch.Tensor, out):
+def _dual_outputs(x: torch.Tensor, out, mfma: bool):
     M, N = x.shape
     if out is not None:
         return out
     kw = dict(dtype=torch.uint8, device=x.device)
+    if mfma:   # flat buffers in the matrix-core scale layout
+        return (torch.empty((M, N), **kw), torch.empty((M * N // 32,), **kw),
+                torch.empty((N, M), **kw), torch.empty((M * N // 32,), **kw))
     return (torch.empty((M, N), **kw), torch.empty((M, N // 32), **kw),
             torch.empty((N, M), **kw), torch.empty((M // 32, N), **kw))
+
+
+def _layout(scale_layout) -> bool:
+    if scale_layout not in ("plain", "mfma"):
+        raise ValueError('scale_layout must be "plain" or "mfma"')
+    return scale_layout == "mfma"
 
 
 def _bf16_matrix(x: torch.Tensor):
@@ -128,23 +144,29 @@ def _bf16_matrix(x: torch.Tensor):
         raise ValueError("x must be a 2-D bf16 tensor with contiguous rows")
 
 
-def mx_quantize_2d_dual(x: torch.Tensor, block_size: int = 32, scaling_mode="rceil", out=None):
+def mx_quantize_2d_dual(x: torch.Tensor, block_size: int = 32, scaling_mode="rceil", out=None,
+                        scale_layout: str = "plain"):
     """Fused dual-axis MXFP8 cast.  Returns uint8 tensors q_row [M,N] (E4M3),
-    s_row [M,N/32] (E8M0), q_col [N,M] (E4M3, transposed), s_col [M/32,N]."""
+    s_row [M,N/32] (E8M0), q_col [N,M] (E4M3, transposed), s_col [M/32,N].
+    With scale_layout="mfma" s_row and s_col are flat [M*N/32] buffers in the
+    matrix-core layout (s_row for the operand [M rows, N/32 blocks], s_col
+    for [N rows, M/32 blocks]), ready for the *_mfma contractions."""
     _bf16_matrix(x)
     M, N = x.shape
-    q_row, s_row, q_col, s_col = _dual_outputs(x, out)
-    _check(_load().mx_quantize_2d_dual(x.data_ptr(), M, N, x.stride(0), block_size, _scaling(scaling_mode),
-                                       q_row.data_ptr(), s_row.data_ptr(), q_col.data_ptr(),
-                                       s_col.data_ptr(), _stream(x.device)))
+    mfma = _layout(scale_layout)
+    q_row, s_row, q_col, s_col = _dual_outputs(x, out, mfma)
+    fn = _load().mx_quantize_2d_dual_mfma if mfma else _load().mx_quantize_2d_dual
+    _check(fn(x.data_ptr(), M, N, x.stride(0), block_size, _scaling(scaling_mode), q_row.data_ptr(),
+              s_row.data_ptr(), q_col.data_ptr(), s_col.data_ptr(), _stream(x.device)))
     return q_row, s_row, q_col, s_col
 
 
 def mx_quantize_grouped(x: torch.Tensor, offs: torch.Tensor, block_size: int = 32, scaling_mode="rceil",
-                        err: torch.Tensor | None = None, out=None):
+                        err: torch.Tensor | None = None, out=None, scale_layout: str = "plain"):
     """Grouped dual-axis cast: the dense outputs, with the colwise scale rows
     of the uncovered tail (rows >= offs[-1]) zeroed.  ``err`` (int32 device
-    tensor of one element) receives the device-side offset check code."""
+    tensor of one element) receives the device-side offset check code.
+    scale_layout as for mx_quantize_2d_dual."""
     _bf16_matrix(x)
     M, N = x.shape
     if offs.dtype != torch.int32 or offs.dim() != 1 or not offs.is_contiguous():
@@ -154,11 +176,12 @@ def mx_quantize_grouped(x: torch.Tensor, offs: torch.Tensor, block_size: int = 3
         _need_cuda(err, "err")
         if err.dtype != torch.int32 or err.numel() != 1:
             raise ValueError("err must be a one-element int32 tensor")
-    q_row, s_row, q_col, s_col = _dual_outputs(x, out)
-    _check(_load().mx_quantize_grouped(x.data_ptr(), M, N, x.stride(0), block_size, _scaling(scaling_mode),
-                                       offs.data_ptr() if offs.numel() else None, offs.numel(),
-                                       q_row.data_ptr(), s_row.data_ptr(), q_col.data_ptr(),
-                                       s_col.data_ptr(), _ptr(err), _stream(x.device)))
+    mfma = _layout(scale_layout)
+    q_row, s_row, q_col, s_col = _dual_outputs(x, out, mfma)
+    fn = _load().mx_quantize_grouped_mfma if mfma else _load().mx_quantize_grouped
+    _check(fn(x.data_ptr(), M, N, x.stride(0), block_size, _scaling(scaling_mode),
+              offs.data_ptr() if offs.numel() else None, offs.numel(), q_row.data_ptr(), s_row.data_ptr(),
+              q_col.data_ptr(), s_col.data_ptr(), _ptr(err), _stream(x.device)))
     return q_row, s_row, q_col, s_col
 
 
@@ -411,6 +434,78 @@ def mx_grouped_gemm_k(A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB: to
     _check(_load().mx_grouped_gemm_k(A.data_ptr(), A.stride(0), sA.data_ptr(), sa[0], sa[1], B.data_ptr(),
                                      B.stride(0), sB.data_ptr(), sb[0], sb[1], offs.data_ptr(), G, M, N, K,
                                      C.data_ptr(), C.stride(1), C.stride(0), _out_code(C.dtype), _stream(A.device)))
+    return C
+
+
+def _mfma_scales(s: torch.Tensor, nbytes: int, name: str):
+    _need_cuda(s, name)
+    if s.dtype != torch.uint8 or not s.is_contiguous() or s.numel() != nbytes:
+        raise ValueError(f"{name} must be a contiguous uint8 buffer of {nbytes} bytes (matrix-core layout)")
+
+
+def mx_gemm_nt_mfma(A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB: torch.Tensor, out_dtype=torch.float32,
+                    out: torch.Tensor | None = None):
+    """mx_gemm_nt with sA, sB in the matrix-core scale layout (flat, M*K/32
+    and N*K/32 bytes): the s_row / s_col of an "mfma" cast."""
+    _codes(A, "A")
+    _codes(B, "B")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("A and B must share the contraction extent")
+    _mfma_scales(sA, M * K // 32, "sA")
+    _mfma_scales(sB, N * K // 32, "sB")
+    C = _gemm_out(out, (M, N), out_dtype, A.device)
+    _check(_load().mx_gemm_nt_mfma(A.data_ptr(), A.stride(0), sA.data_ptr(), B.data_ptr(), B.stride(0),
+                                   sB.data_ptr(), M, N, K, C.data_ptr(), C.stride(0), _out_code(C.dtype),
+                                   _stream(A.device)))
+    return C
+
+
+def mx_grouped_gemm_rows_mfma(A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB: torch.Tensor,
+                              offs: torch.Tensor, out_dtype=torch.float32, out: torch.Tensor | None = None):
+    """mx_grouped_gemm_rows with matrix-core scale layouts: sA flat
+    [M*K/32], sB [E, N*K/32] (expert e's scales in row e)."""
+    _codes(A, "A")
+    M, K = A.shape
+    if B.dim() != 3 or B.stride(2) != 1 or B.shape[2] != K:
+        raise ValueError("B must be [E, N, K] codes with contiguous rows")
+    E, N = B.shape[0], B.shape[1]
+    _need_cuda(sB, "sB")
+    if sB.dtype != torch.uint8 or sB.dim() != 2 or tuple(sB.shape) != (E, N * K // 32) or sB.stride(1) != 1:
+        raise ValueError("sB must be a uint8 [E, N*K/32] tensor with contiguous rows")
+    if offs.dtype != torch.int32 or offs.dim() != 1 or not offs.is_contiguous() or offs.numel() > E:
+        raise ValueError("offs must be a contiguous int32 [G] tensor with G <= E")
+    _need_cuda(offs, "offs")
+    _mfma_scales(sA, M * K // 32, "sA")
+    C = _gemm_out(out, (M, N), out_dtype, A.device)
+    _check(_load().mx_grouped_gemm_rows_mfma(A.data_ptr(), A.stride(0), sA.data_ptr(), B.data_ptr(), B.stride(1),
+                                             B.stride(0), sB.data_ptr(), sB.stride(0), offs.data_ptr(),
+                                             offs.numel(), M, N, K, C.data_ptr(), C.stride(0), _out_code(C.dtype),
+                                             _stream(A.device)))
+    return C
+
+
+def mx_grouped_gemm_k_mfma(A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB: torch.Tensor,
+                           offs: torch.Tensor, out_dtype=torch.float32, out: torch.Tensor | None = None):
+    """mx_grouped_gemm_k with sA [M*K/32], sB [N*K/32] in the matrix-core
+    scale layout (the s_col of an "mfma" cast of each token-major operand)."""
+    _codes(A, "A")
+    _codes(B, "B")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("A and B must share the contraction extent")
+    if offs.dtype != torch.int32 or offs.dim() != 1 or not offs.is_contiguous():
+        raise ValueError("offs must be a contiguous int32 [G] tensor")
+    _need_cuda(offs, "offs")
+    _mfma_scales(sA, M * K // 32, "sA")
+    _mfma_scales(sB, N * K // 32, "sB")
+    G = offs.numel()
+    C = _gemm_out(out, (G, M, N), out_dtype, A.device)
+    _check(_load().mx_grouped_gemm_k_mfma(A.data_ptr(), A.stride(0), sA.data_ptr(), B.data_ptr(), B.stride(0),
+                                          sB.data_ptr(), offs.data_ptr(), G, M, N, K, C.data_ptr(), C.stride(1),
+                                          C.stride(0), _out_code(C.dtype), _stream(A.device)))
     return C
 
 

@@ -55,6 +55,18 @@
 //              call still runs).  Measured on MI355X with rotating buffers:
 //              the bf16 [32768, 8192] call runs in 193 us instead of 213 us
 //              with ordinary accesses, [8192, 7168] in 43.5 us instead of 53.6.
+//   * matrix-core scale layout (optional): both scale tensors written in
+//              the order in which the scaled 16x16x128 matrix instruction
+//              takes them, so a contraction reads one dword per lane and
+//              128-wide step.  For an operand with R rows and kb = K/32 blocks
+//              per row, scale (r, b) sits at byte
+//                ((r/64 * kb/4 + b/4) * 64 + 16 (b%4) + r%16) * 4 + (r%64)/16,
+//              i.e. a 64-row group and a 4-block step own 256 contiguous
+//              bytes, one dword per lane.  s_row is the operand [M rows, N/32
+//              blocks]; s_col belongs to q_col, the operand [N rows, M/32
+//              blocks].  A tile owns exactly two such runs of each tensor, so
+//              it stages its scale bytes in LDS and writes four 256-byte runs;
+//              no second pass is needed.
 //   * offsets: per-tile bases are uniform buffer resources and per-lane
 //              offsets are 32-bit, which the host guarantees by limiting M, N
 //              and the row pitch to 2^24.
@@ -69,6 +81,11 @@ constexpr int kTile = 128;
 constexpr int kThreads = 256;
 constexpr int64_t kMaxStagedN = 16256;   // 127 tiles x 129 dwords = 65,532 bytes of LDS
 constexpr double kMemorySideCacheBytes = 256.0 * 1024 * 1024;   // MI355X last-level (MALL) capacity
+
+// How a call writes s_row (s_col is plain unless the matrix-core layout is asked for).
+constexpr int kScalesDirect = 0;   // [M][N/32], 4-byte stores per tile row
+constexpr int kScalesStaged = 1;   // [M][N/32], contiguous per-tile runs put in order by srow_permute_kernel
+constexpr int kScalesMfma = 2;     // both tensors in the matrix-core layout
 
 typedef short v2i16 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -154,7 +171,14 @@ __device__ void validate_offsets(const int32_t* offs, int32_t G, int64_t M, int3
     if (threadIdx.x == 0) *err = first_bad == INT_MAX ? 0 : offs_code(offs, first_bad, M);
 }
 
-template <bool kGrouped, bool kStage>
+// Byte of the tile's 512-byte staging run for local row r (0..127) and local
+// block j (0..3) in the matrix-core scale layout: run r/64, then lane
+// 16 j + r%16, byte (r%64)/16 of its dword.
+__device__ __forceinline__ uint32_t mfma_scale_slot(uint32_t r, uint32_t j) {
+    return (r >> 6) * 256u + (16u * j + (r & 15u)) * 4u + ((r >> 4) & 3u);
+}
+
+template <bool kGrouped, int kScales>
 __global__ __launch_bounds__(kThreads)
 void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, int64_t N,
                       uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
@@ -162,7 +186,8 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
                       uint32_t tiles_n, uint32_t tiles, uint32_t row_stream_mask, bool diagonal,
                       const int32_t* __restrict__ offs, int32_t G, int32_t* __restrict__ err) {
     __shared__ uint4 lds_tile[kTile * 16];     // [128 rows][16 x 16 bytes]
-    __shared__ uint32_t lds_srow[kTile];       // the tile's 4 rowwise scale bytes per row
+    __shared__ uint32_t lds_srow[kTile];       // the tile's 512 rowwise scale bytes
+    __shared__ uint32_t lds_scol[kTile];       // the tile's 512 colwise scale bytes (matrix-core layout)
 
     const uint32_t t = threadIdx.x;
     const uint32_t bid = blockIdx.x;
@@ -217,11 +242,20 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
         const uint32_t off = r * uint32_t(N) + c8;
         if (stream_row) __builtin_amdgcn_raw_buffer_store_b64(o, rq_row, off, 0, kPolicyStream);
         else __builtin_amdgcn_raw_buffer_store_b64(o, rq_row, off, 0, kPolicyDefault);
-        if ((t & 3u) == 0u) reinterpret_cast<uint8_t*>(lds_srow)[r * 4u + ((t & 15u) >> 2)] = uint8_t(b);
+        if ((t & 3u) == 0u) {
+            const uint32_t j = (t & 15u) >> 2;
+            reinterpret_cast<uint8_t*>(lds_srow)[kScales == kScalesMfma ? mfma_scale_slot(r, j) : r * 4u + j] = uint8_t(b);
+        }
     }
     __syncthreads();
 
-    if (kStage) {
+    if (kScales == kScalesMfma) {
+        // runs (2 tm + h) * tiles_n + tn of the [M rows, N/32 blocks] operand, h = 0, 1
+        if (t < 32) {
+            const int64_t run = (2 * int64_t(tm) + (t >> 4)) * tiles_n + tn;
+            *reinterpret_cast<uint4*>(s_row + run * 256 + 16 * (t & 15u)) = reinterpret_cast<const uint4*>(lds_srow)[t];
+        }
+    } else if (kScales == kScalesStaged) {
         // Sector-complete staging: the 8 tiles of a group share the 128 x 32-byte
         // s_row region of their rows; tile jt writes its 512 bytes as pieces
         // 16*jt .. 16*jt+15 (piece P = the region's row P, 8 of this tile's rows
@@ -278,9 +312,23 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
         __builtin_amdgcn_raw_buffer_store_b128(hi, rq_col, off + uint32_t(M), 0, kPolicyStream);
         if ((c & 1u) == 0u) {
             const int64_t sbr = m0 / 32 + (c >> 1);
-            uint16_t sv = uint16_t(b_lo | (b_hi << 8));
-            if (kGrouped && sbr >= tail_br) sv = 0;
-            *reinterpret_cast<uint16_t*>(s_col + sbr * N + n0 + 2 * cp) = sv;
+            const bool tail = kGrouped && sbr >= tail_br;
+            if (kScales == kScalesMfma) {
+                uint8_t* ls = reinterpret_cast<uint8_t*>(lds_scol);
+                ls[mfma_scale_slot(2u * cp, c >> 1)] = tail ? uint8_t(0) : uint8_t(b_lo);
+                ls[mfma_scale_slot(2u * cp + 1u, c >> 1)] = tail ? uint8_t(0) : uint8_t(b_hi);
+            } else {
+                const uint16_t sv = tail ? uint16_t(0) : uint16_t(b_lo | (b_hi << 8));
+                *reinterpret_cast<uint16_t*>(s_col + sbr * N + n0 + 2 * cp) = sv;
+            }
+        }
+    }
+    if (kScales == kScalesMfma) {
+        // runs (2 tn + h) * tiles_m + tm of the [N rows, M/32 blocks] operand
+        __syncthreads();
+        if (t < 32) {
+            const int64_t run = (2 * int64_t(tn) + (t >> 4)) * tiles_m + tm;
+            *reinterpret_cast<uint4*>(s_col + run * 256 + 16 * (t & 15u)) = reinterpret_cast<const uint4*>(lds_scol)[t];
         }
     }
 }
@@ -328,30 +376,37 @@ void offs_validate_kernel(const int32_t* __restrict__ offs, int32_t G, int64_t M
 hipError_t launch_dual_axis(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x,
                             uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
                             const int32_t* offs, int32_t G, int32_t* err, bool grouped,
-                            hipStream_t stream) {
+                            bool mfma_scales, hipStream_t stream) {
     const uint32_t tiles_n = uint32_t(N / kTile);
     const uint32_t tiles = uint32_t((M / kTile) * (N / kTile));
-    // the band fits the permute pass's LDS, and its chunks hold 4 whole tiles
-    const bool stage = N <= kMaxStagedN && N % 512 == 0;
+    // the staged s_row layout needs the band to fit the permute pass's LDS
+    // and its chunks to hold 4 whole tiles
+    const int scales = mfma_scales ? kScalesMfma
+                       : (N <= kMaxStagedN && N % 512 == 0) ? kScalesStaged : kScalesDirect;
     // q_row streaming share by the call's size against the memory-side cache
     const double call_bytes = 4.0625 * double(M) * double(N);
     const bool large = call_bytes > 2.0 * kMemorySideCacheBytes;
     const uint32_t row_stream = large ? 0x3Fu : 0x00u;
-    const int32_t* no_offs = nullptr;
-    int32_t* no_err = nullptr;
-    if (grouped && stage)
-        hipLaunchKernelGGL((dual_axis_kernel<true, true>), dim3(tiles), dim3(kThreads), 0, stream,
-                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles, row_stream, large, offs, G, err);
-    else if (grouped)
-        hipLaunchKernelGGL((dual_axis_kernel<true, false>), dim3(tiles), dim3(kThreads), 0, stream,
-                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles, row_stream, large, offs, G, err);
-    else if (stage)
-        hipLaunchKernelGGL((dual_axis_kernel<false, true>), dim3(tiles), dim3(kThreads), 0, stream,
-                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles, row_stream, large, no_offs, 0, no_err);
-    else
-        hipLaunchKernelGGL((dual_axis_kernel<false, false>), dim3(tiles), dim3(kThreads), 0, stream,
-                           x, ld_x, M, N, q_row, s_row, q_col, s_col, tiles_n, tiles, row_stream, large, no_offs, 0, no_err);
-    if (stage) {
+    if (!grouped) {
+        offs = nullptr;
+        G = 0;
+        err = nullptr;
+    }
+    const dim3 grid(tiles), block(kThreads);
+#define MXQ_LAUNCH(GR, SC)                                                                                   \
+    hipLaunchKernelGGL((dual_axis_kernel<GR, SC>), grid, block, 0, stream, x, ld_x, M, N, q_row, s_row, q_col, \
+                       s_col, tiles_n, tiles, row_stream, large, offs, G, err)
+    if (grouped) {
+        if (scales == kScalesMfma) MXQ_LAUNCH(true, kScalesMfma);
+        else if (scales == kScalesStaged) MXQ_LAUNCH(true, kScalesStaged);
+        else MXQ_LAUNCH(true, kScalesDirect);
+    } else {
+        if (scales == kScalesMfma) MXQ_LAUNCH(false, kScalesMfma);
+        else if (scales == kScalesStaged) MXQ_LAUNCH(false, kScalesStaged);
+        else MXQ_LAUNCH(false, kScalesDirect);
+    }
+#undef MXQ_LAUNCH
+    if (scales == kScalesStaged) {
         const uint32_t lds = uint32_t(N / kTile) * 129u * 4u;
         hipLaunchKernelGGL(srow_permute_kernel, dim3(uint32_t(M / kTile)), dim3(kPermThreads), lds, stream, s_row, N);
     }

@@ -29,7 +29,11 @@
 //   * scales: a lane needs one A byte per 16-row sub-tile and one B byte per
 //     16-column sub-tile per step; the four A bytes (and the four B bytes)
 //     are packed into one register and the instruction's op_sel picks the
-//     byte.  They are fetched one step ahead, like the data.
+//     byte.  They are fetched one step ahead, like the data.  From strided
+//     scale views (the cast's plain layouts) that takes four byte loads per
+//     operand; from the matrix-core scale layout (scale (r, b) at byte
+//     ((r/64 * K/128 + b/4) * 64 + 16 (b%4) + r%16) * 4 + (r%64)/16) the
+//     register is one dword, and a wave's 64 dwords are one 256-byte run.
 //   * groups: row groups (the forward: rows of group g use expert g's
 //     operand, rows past the last offset give 0) find their group from the
 //     tile's first row, since groups are multiples of 128 rows; contraction
@@ -50,7 +54,7 @@ struct GemmArgs {
     const uint8_t* A;
     int64_t lda;
     const uint8_t* sA;
-    int64_t sa_rs, sa_bs;
+    int64_t sa_rs, sa_bs;     // strided view; in the matrix-core layout sa_rs is the bytes per 64 rows
     const uint8_t* B;
     int64_t ldb, b_gs;
     const uint8_t* sB;
@@ -84,7 +88,7 @@ __device__ __forceinline__ int64_t clamp_end(int64_t v, int64_t lo, int64_t hi) 
     return v - (v - lo) % kTile;
 }
 
-template <int kOut>
+template <int kOut, bool kMfmaScales>
 __global__ __launch_bounds__(kThreads, 2)
 void mx_gemm_kernel(GemmArgs p) {
     __shared__ uint4 lds[2][2][kTile * 8];      // [buffer][A, B][row * 8 + chunk]
@@ -137,6 +141,9 @@ void mx_gemm_kernel(GemmArgs p) {
         const uint8_t* sa_row = p.sA + (m0 + wm * 64 + (lane & 15u)) * p.sa_rs;
         const uint8_t* sb_row = sB + (n0 + wn * 64 + (lane & 15u)) * p.sb_rs;
         const int64_t kgrp = int64_t(lane >> 4);                   // the lane's 32-wide k-block of a step
+        // matrix-core layout: this lane's dword of its 64-row group, one 256-byte run per step
+        const uint32_t* sa_run = reinterpret_cast<const uint32_t*>(p.sA + int64_t(2 * tm + wm) * p.sa_rs) + lane;
+        const uint32_t* sb_run = reinterpret_cast<const uint32_t*>(sB + int64_t(2 * tn + wn) * p.sb_rs) + lane;
         // this thread's four staging chunks: c = t + 256 i, row c / 8, 16-byte piece c % 8
         const uint32_t r0 = t >> 3, ch = t & 7u;                    // rows r0, r0 + 32, r0 + 64, r0 + 96
         const uint8_t* ga = p.A + (m0 + r0) * p.lda + 16 * ch;
@@ -153,14 +160,19 @@ void mx_gemm_kernel(GemmArgs p) {
             rb1 = *reinterpret_cast<const uint4*>(gb + ldb32 + (k));                          \
             rb2 = *reinterpret_cast<const uint4*>(gb + 2 * ldb32 + (k));                      \
             rb3 = *reinterpret_cast<const uint4*>(gb + 3 * ldb32 + (k));                      \
-            const int64_t blk_ = (k) / 32 + kgrp;                                             \
-            uint32_t a4_ = 0, b4_ = 0;                                                        \
-            for (int s_ = 0; s_ < 4; ++s_) {                                                  \
-                a4_ |= uint32_t(sa_row[16 * s_ * p.sa_rs + blk_ * p.sa_bs]) << (8 * s_);      \
-                b4_ |= uint32_t(sb_row[16 * s_ * p.sb_rs + blk_ * p.sb_bs]) << (8 * s_);      \
+            if (kMfmaScales) {                                                                \
+                SA = int(sa_run[((k) / kTile) * 64]);                                         \
+                SB = int(sb_run[((k) / kTile) * 64]);                                         \
+            } else {                                                                          \
+                const int64_t blk_ = (k) / 32 + kgrp;                                         \
+                uint32_t a4_ = 0, b4_ = 0;                                                    \
+                for (int s_ = 0; s_ < 4; ++s_) {                                              \
+                    a4_ |= uint32_t(sa_row[16 * s_ * p.sa_rs + blk_ * p.sa_bs]) << (8 * s_);  \
+                    b4_ |= uint32_t(sb_row[16 * s_ * p.sb_rs + blk_ * p.sb_bs]) << (8 * s_);  \
+                }                                                                             \
+                SA = int(a4_);                                                                \
+                SB = int(b4_);                                                                \
             }                                                                                 \
-            SA = int(a4_);                                                                    \
-            SB = int(b4_);                                                                    \
         } while (0)
 #define MXQ_STORE_STEP(buf)                                                                   \
         do {                                                                                  \
@@ -234,17 +246,29 @@ void mx_gemm_kernel(GemmArgs p) {
 hipError_t launch_mx_gemm(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, int64_t sa_bs,
                           const uint8_t* B, int64_t ldb, int64_t b_gs, const uint8_t* sB, int64_t sb_rs,
                           int64_t sb_bs, int64_t sb_gs, void* C, int64_t ldc, int64_t c_gs, int64_t M, int64_t N,
-                          int64_t K, const int32_t* offs, int32_t G, int mode, int out_dtype, hipStream_t stream) {
+                          int64_t K, const int32_t* offs, int32_t G, int mode, int out_dtype, bool mfma_scales,
+                          hipStream_t stream) {
     GemmArgs p;
     p.A = A; p.lda = lda; p.sA = sA; p.sa_rs = sa_rs; p.sa_bs = sa_bs;
     p.B = B; p.ldb = ldb; p.b_gs = b_gs; p.sB = sB; p.sb_rs = sb_rs; p.sb_bs = sb_bs; p.sb_gs = sb_gs;
     p.C = C; p.ldc = ldc; p.c_gs = c_gs;
     p.M = M; p.N = N; p.K = K; p.offs = offs; p.G = G; p.mode = mode;
+    if (mfma_scales) {
+        // the K/32 scale bytes of each of 64 rows
+        p.sa_rs = p.sb_rs = 2 * K;
+        p.sa_bs = p.sb_bs = 0;
+    }
     p.tiles_m = uint32_t(M / kTile);
     p.tiles_n = uint32_t(N / kTile);
     const uint32_t tiles = p.tiles_m * p.tiles_n * uint32_t(mode == 1 ? G : 1);
-    if (out_dtype == 0) hipLaunchKernelGGL(mx_gemm_kernel<0>, dim3(tiles), dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL(mx_gemm_kernel<1>, dim3(tiles), dim3(kThreads), 0, stream, p);
+    const dim3 grid(tiles), block(kThreads);
+    if (out_dtype == 0) {
+        if (mfma_scales) hipLaunchKernelGGL((mx_gemm_kernel<0, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((mx_gemm_kernel<0, false>), grid, block, 0, stream, p);
+    } else {
+        if (mfma_scales) hipLaunchKernelGGL((mx_gemm_kernel<1, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((mx_gemm_kernel<1, false>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 

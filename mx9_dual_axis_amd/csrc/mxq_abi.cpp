@@ -61,6 +61,45 @@ int check_dual(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x, int32_t bl
     return MX_OK;
 }
 
+int dual_call(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x, int32_t block_size,
+              int32_t scaling_mode, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+              bool mfma_scales, void* stream) {
+    int rc = check_dual(x, M, N, ld_x, block_size, scaling_mode, q_row, s_row, q_col, s_col);
+    if (rc != MX_OK) return rc;
+    const uint64_t mn = uint64_t(M) * uint64_t(N);
+    const Span s[5] = {{addr(x), matrix_bytes(M, N, ld_x, 2)}, {addr(q_row), mn}, {addr(s_row), mn / 32},
+                       {addr(q_col), mn}, {addr(s_col), mn / 32}};
+    if (any_overlap(s, 5)) return MX_E_OVERLAP;
+    if (M == 0 || N == 0) return MX_OK;
+    hipError_t e = mxq::launch_dual_axis(x, M, N, ld_x, q_row, s_row, q_col, s_col, nullptr, 0, nullptr, false,
+                                         mfma_scales, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+}
+
+int grouped_call(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x, int32_t block_size,
+                 int32_t scaling_mode, const int32_t* offs, int32_t G, uint8_t* q_row, uint8_t* s_row,
+                 uint8_t* q_col, uint8_t* s_col, int32_t* err, bool mfma_scales, void* stream) {
+    int rc = check_dual(x, M, N, ld_x, block_size, scaling_mode, q_row, s_row, q_col, s_col);
+    if (rc != MX_OK) return rc;
+    if (G < 0) return MX_E_SHAPE;
+    if (G > 0 && !offs) return MX_E_NULL;
+    if (G > 0 && !aligned(offs, 4)) return MX_E_ALIGN;
+    if (err && !aligned(err, 4)) return MX_E_ALIGN;
+    const uint64_t mn = uint64_t(M) * uint64_t(N);
+    const Span s[7] = {{addr(x), matrix_bytes(M, N, ld_x, 2)}, {addr(q_row), mn}, {addr(s_row), mn / 32},
+                       {addr(q_col), mn}, {addr(s_col), mn / 32},
+                       {addr(offs), G > 0 ? uint64_t(G) * 4 : 0}, {addr(err), err ? 4u : 0u}};
+    if (any_overlap(s, 7)) return MX_E_OVERLAP;
+    hipError_t e = hipSuccess;
+    if (M == 0 || N == 0) {
+        if (err) e = mxq::launch_offs_validate(offs, G, M, err, static_cast<hipStream_t>(stream));
+    } else {
+        e = mxq::launch_dual_axis(x, M, N, ld_x, q_row, s_row, q_col, s_col, offs, G, err, true, mfma_scales,
+                                  static_cast<hipStream_t>(stream));
+    }
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+}
+
 // Shared checks of the axis and record calls; nb receives the block count.
 int check_mx9_view(int32_t dtype, int64_t outer, int64_t len, int64_t inner, int32_t block_size,
                    uint64_t* nb) {
@@ -87,7 +126,7 @@ constexpr int64_t kMaxGemm = int64_t(1) << 24;
 // scale strides, the output type and pitch.  K is the contraction extent.
 int check_gemm(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, int64_t sa_bs,
                const uint8_t* B, int64_t ldb, const uint8_t* sB, int64_t sb_rs, int64_t sb_bs,
-               int64_t M, int64_t N, int64_t K, const void* C, int64_t ldc, int32_t out_dtype) {
+               int64_t M, int64_t N, int64_t K, const void* C, int64_t ldc, int32_t out_dtype, bool mfma) {
     const bool empty = M == 0 || N == 0;
     if (!empty && (!A || !sA || !B || !sB || !C)) return MX_E_NULL;
     if (out_dtype != MX_DTYPE_F32 && out_dtype != MX_DTYPE_BF16) return MX_E_DTYPE;
@@ -99,7 +138,80 @@ int check_gemm(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, 
         return MX_E_STRIDE;
     const uintptr_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
     if (!empty && (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, esz))) return MX_E_ALIGN;
+    if (!empty && mfma && (!aligned(sA, 16) || !aligned(sB, 16))) return MX_E_ALIGN;
     return MX_OK;
+}
+
+// Bytes of one operand's scales: a strided view, or rows * K/32 in the matrix-core layout.
+uint64_t scale_bytes(bool mfma, int64_t rows, int64_t K, int64_t rs, int64_t bs) {
+    return mfma ? uint64_t(rows) * uint64_t(K / 32) : scale_span(rows, K / 32, rs, bs);
+}
+
+int gemm_call(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, int64_t sa_bs,
+              const uint8_t* B, int64_t ldb, const uint8_t* sB, int64_t sb_rs, int64_t sb_bs,
+              int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, int32_t out_dtype, bool mfma, void* stream) {
+    int rc = check_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, sB, sb_rs, sb_bs, M, N, K, C, ldc, out_dtype, mfma);
+    if (rc != MX_OK) return rc;
+    const uint64_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
+    const uint64_t cb = matrix_bytes(M, N, ldc, int64_t(esz));
+    const Span s[5] = {{addr(C), cb}, {addr(A), matrix_bytes(M, K, lda, 1)}, {addr(B), matrix_bytes(N, K, ldb, 1)},
+                       {addr(sA), scale_bytes(mfma, M, K, sa_rs, sa_bs)}, {addr(sB), scale_bytes(mfma, N, K, sb_rs, sb_bs)}};
+    for (int i = 1; i < 5; ++i)
+        if (overlap(s[0], s[i])) return MX_E_OVERLAP;
+    if (M == 0 || N == 0) return MX_OK;
+    hipError_t e = mxq::launch_mx_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, 0, sB, sb_rs, sb_bs, 0, C, ldc, 0, M, N, K,
+                                       nullptr, 1, 0, out_dtype, mfma, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+}
+
+int gemm_rows_call(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, int64_t sa_bs,
+                   const uint8_t* B, int64_t ldb, int64_t b_gs, const uint8_t* sB, int64_t sb_rs,
+                   int64_t sb_bs, int64_t sb_gs, const int32_t* offs, int32_t G, int64_t M, int64_t N,
+                   int64_t K, void* C, int64_t ldc, int32_t out_dtype, bool mfma, void* stream) {
+    int rc = check_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, sB, sb_rs, sb_bs, M, N, K, C, ldc, out_dtype, mfma);
+    if (rc != MX_OK) return rc;
+    if (G < 1 || G > (1 << 20)) return MX_E_SHAPE;
+    if (!offs) return MX_E_NULL;
+    if (!aligned(offs, 4)) return MX_E_ALIGN;
+    if (b_gs < 0 || sb_gs < 0) return MX_E_STRIDE;
+    const uint64_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
+    const Span s[6] = {{addr(C), matrix_bytes(M, N, ldc, int64_t(esz))}, {addr(A), matrix_bytes(M, K, lda, 1)},
+                       {addr(B), uint64_t(G - 1) * uint64_t(b_gs) + matrix_bytes(N, K, ldb, 1)},
+                       {addr(sA), scale_bytes(mfma, M, K, sa_rs, sa_bs)},
+                       {addr(sB), uint64_t(G - 1) * uint64_t(sb_gs) + scale_bytes(mfma, N, K, sb_rs, sb_bs)},
+                       {addr(offs), uint64_t(G) * 4}};
+    for (int i = 1; i < 6; ++i)
+        if (overlap(s[0], s[i])) return MX_E_OVERLAP;
+    if (M == 0 || N == 0) return MX_OK;
+    hipError_t e = mxq::launch_mx_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, b_gs, sB, sb_rs, sb_bs, sb_gs, C, ldc, 0,
+                                       M, N, K, offs, G, 0, out_dtype, mfma, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+}
+
+int gemm_k_call(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, int64_t sa_bs,
+                const uint8_t* B, int64_t ldb, const uint8_t* sB, int64_t sb_rs, int64_t sb_bs,
+                const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* C, int64_t ldc,
+                int64_t c_gs, int32_t out_dtype, bool mfma, void* stream) {
+    int rc = check_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, sB, sb_rs, sb_bs, M, N, K, C, ldc, out_dtype, mfma);
+    if (rc != MX_OK) return rc;
+    if (G < 1 || G > (1 << 20)) return MX_E_SHAPE;
+    if (!offs) return MX_E_NULL;
+    if (!aligned(offs, 4)) return MX_E_ALIGN;
+    const uint64_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
+    const uint64_t slab = matrix_bytes(M, N, ldc, 1);                  // elements of one group's C
+    if (c_gs < int64_t(slab)) return MX_E_STRIDE;
+    const uint64_t tiles = uint64_t(M / 128) * uint64_t(N / 128) * uint64_t(G);
+    if (tiles > 0x7FFFFFFFull) return MX_E_SHAPE;
+    const Span s[6] = {{addr(C), (uint64_t(G - 1) * uint64_t(c_gs) + slab) * esz},
+                       {addr(A), matrix_bytes(M, K, lda, 1)}, {addr(B), matrix_bytes(N, K, ldb, 1)},
+                       {addr(sA), scale_bytes(mfma, M, K, sa_rs, sa_bs)}, {addr(sB), scale_bytes(mfma, N, K, sb_rs, sb_bs)},
+                       {addr(offs), uint64_t(G) * 4}};
+    for (int i = 1; i < 6; ++i)
+        if (overlap(s[0], s[i])) return MX_E_OVERLAP;
+    if (M == 0 || N == 0) return MX_OK;
+    hipError_t e = mxq::launch_mx_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, 0, sB, sb_rs, sb_bs, 0, C, ldc, c_gs, M, N,
+                                       K, offs, G, 1, out_dtype, mfma, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
 }
 
 }  // namespace
@@ -126,16 +238,14 @@ int mx_quantize_2d_dual(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x,
                         int32_t block_size, int32_t scaling_mode,
                         uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
                         void* stream) {
-    int rc = check_dual(x, M, N, ld_x, block_size, scaling_mode, q_row, s_row, q_col, s_col);
-    if (rc != MX_OK) return rc;
-    const uint64_t mn = uint64_t(M) * uint64_t(N);
-    const Span s[5] = {{addr(x), matrix_bytes(M, N, ld_x, 2)}, {addr(q_row), mn}, {addr(s_row), mn / 32},
-                       {addr(q_col), mn}, {addr(s_col), mn / 32}};
-    if (any_overlap(s, 5)) return MX_E_OVERLAP;
-    if (M == 0 || N == 0) return MX_OK;
-    hipError_t e = mxq::launch_dual_axis(x, M, N, ld_x, q_row, s_row, q_col, s_col, nullptr, 0,
-                                         nullptr, false, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+    return dual_call(x, M, N, ld_x, block_size, scaling_mode, q_row, s_row, q_col, s_col, false, stream);
+}
+
+int mx_quantize_2d_dual_mfma(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x,
+                             int32_t block_size, int32_t scaling_mode,
+                             uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                             void* stream) {
+    return dual_call(x, M, N, ld_x, block_size, scaling_mode, q_row, s_row, q_col, s_col, true, stream);
 }
 
 int mx_quantize_grouped(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x,
@@ -143,25 +253,17 @@ int mx_quantize_grouped(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x,
                         const int32_t* offs, int32_t G,
                         uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
                         int32_t* err, void* stream) {
-    int rc = check_dual(x, M, N, ld_x, block_size, scaling_mode, q_row, s_row, q_col, s_col);
-    if (rc != MX_OK) return rc;
-    if (G < 0) return MX_E_SHAPE;
-    if (G > 0 && !offs) return MX_E_NULL;
-    if (G > 0 && !aligned(offs, 4)) return MX_E_ALIGN;
-    if (err && !aligned(err, 4)) return MX_E_ALIGN;
-    const uint64_t mn = uint64_t(M) * uint64_t(N);
-    const Span s[7] = {{addr(x), matrix_bytes(M, N, ld_x, 2)}, {addr(q_row), mn}, {addr(s_row), mn / 32},
-                       {addr(q_col), mn}, {addr(s_col), mn / 32},
-                       {addr(offs), G > 0 ? uint64_t(G) * 4 : 0}, {addr(err), err ? 4u : 0u}};
-    if (any_overlap(s, 7)) return MX_E_OVERLAP;
-    hipError_t e = hipSuccess;
-    if (M == 0 || N == 0) {
-        if (err) e = mxq::launch_offs_validate(offs, G, M, err, static_cast<hipStream_t>(stream));
-    } else {
-        e = mxq::launch_dual_axis(x, M, N, ld_x, q_row, s_row, q_col, s_col, offs, G, err, true,
-                                  static_cast<hipStream_t>(stream));
-    }
-    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+    return grouped_call(x, M, N, ld_x, block_size, scaling_mode, offs, G, q_row, s_row, q_col, s_col, err,
+                        false, stream);
+}
+
+int mx_quantize_grouped_mfma(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x,
+                             int32_t block_size, int32_t scaling_mode,
+                             const int32_t* offs, int32_t G,
+                             uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                             int32_t* err, void* stream) {
+    return grouped_call(x, M, N, ld_x, block_size, scaling_mode, offs, G, q_row, s_row, q_col, s_col, err,
+                        true, stream);
 }
 
 int mx9_pack(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld_x,
@@ -288,68 +390,43 @@ int mx9_unpack_records(const uint8_t* packed, int64_t ld_p, int64_t outer, int64
 int mx_gemm_nt(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, int64_t sa_bs,
                const uint8_t* B, int64_t ldb, const uint8_t* sB, int64_t sb_rs, int64_t sb_bs,
                int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, int32_t out_dtype, void* stream) {
-    int rc = check_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, sB, sb_rs, sb_bs, M, N, K, C, ldc, out_dtype);
-    if (rc != MX_OK) return rc;
-    const uint64_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
-    const uint64_t cb = matrix_bytes(M, N, ldc, int64_t(esz));
-    const Span s[5] = {{addr(C), cb}, {addr(A), matrix_bytes(M, K, lda, 1)}, {addr(B), matrix_bytes(N, K, ldb, 1)},
-                       {addr(sA), scale_span(M, K / 32, sa_rs, sa_bs)}, {addr(sB), scale_span(N, K / 32, sb_rs, sb_bs)}};
-    for (int i = 1; i < 5; ++i)
-        if (overlap(s[0], s[i])) return MX_E_OVERLAP;
-    if (M == 0 || N == 0) return MX_OK;
-    hipError_t e = mxq::launch_mx_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, 0, sB, sb_rs, sb_bs, 0, C, ldc, 0, M, N, K,
-                                       nullptr, 1, 0, out_dtype, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+    return gemm_call(A, lda, sA, sa_rs, sa_bs, B, ldb, sB, sb_rs, sb_bs, M, N, K, C, ldc, out_dtype, false, stream);
+}
+
+int mx_gemm_nt_mfma(const uint8_t* A, int64_t lda, const uint8_t* sA, const uint8_t* B, int64_t ldb,
+                    const uint8_t* sB, int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, int32_t out_dtype,
+                    void* stream) {
+    return gemm_call(A, lda, sA, 0, 0, B, ldb, sB, 0, 0, M, N, K, C, ldc, out_dtype, true, stream);
 }
 
 int mx_grouped_gemm_rows(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, int64_t sa_bs,
                          const uint8_t* B, int64_t ldb, int64_t b_gs, const uint8_t* sB, int64_t sb_rs,
                          int64_t sb_bs, int64_t sb_gs, const int32_t* offs, int32_t G, int64_t M, int64_t N,
                          int64_t K, void* C, int64_t ldc, int32_t out_dtype, void* stream) {
-    int rc = check_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, sB, sb_rs, sb_bs, M, N, K, C, ldc, out_dtype);
-    if (rc != MX_OK) return rc;
-    if (G < 1 || G > (1 << 20)) return MX_E_SHAPE;
-    if (!offs) return MX_E_NULL;
-    if (!aligned(offs, 4)) return MX_E_ALIGN;
-    if (b_gs < 0 || sb_gs < 0) return MX_E_STRIDE;
-    const uint64_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
-    const Span s[6] = {{addr(C), matrix_bytes(M, N, ldc, int64_t(esz))}, {addr(A), matrix_bytes(M, K, lda, 1)},
-                       {addr(B), uint64_t(G - 1) * uint64_t(b_gs) + matrix_bytes(N, K, ldb, 1)},
-                       {addr(sA), scale_span(M, K / 32, sa_rs, sa_bs)},
-                       {addr(sB), uint64_t(G - 1) * uint64_t(sb_gs) + scale_span(N, K / 32, sb_rs, sb_bs)},
-                       {addr(offs), uint64_t(G) * 4}};
-    for (int i = 1; i < 6; ++i)
-        if (overlap(s[0], s[i])) return MX_E_OVERLAP;
-    if (M == 0 || N == 0) return MX_OK;
-    hipError_t e = mxq::launch_mx_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, b_gs, sB, sb_rs, sb_bs, sb_gs, C, ldc, 0,
-                                       M, N, K, offs, G, 0, out_dtype, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+    return gemm_rows_call(A, lda, sA, sa_rs, sa_bs, B, ldb, b_gs, sB, sb_rs, sb_bs, sb_gs, offs, G, M, N, K, C,
+                          ldc, out_dtype, false, stream);
+}
+
+int mx_grouped_gemm_rows_mfma(const uint8_t* A, int64_t lda, const uint8_t* sA, const uint8_t* B, int64_t ldb,
+                              int64_t b_gs, const uint8_t* sB, int64_t sb_gs, const int32_t* offs, int32_t G,
+                              int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, int32_t out_dtype,
+                              void* stream) {
+    return gemm_rows_call(A, lda, sA, 0, 0, B, ldb, b_gs, sB, 0, 0, sb_gs, offs, G, M, N, K, C, ldc, out_dtype,
+                          true, stream);
 }
 
 int mx_grouped_gemm_k(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, int64_t sa_bs,
                       const uint8_t* B, int64_t ldb, const uint8_t* sB, int64_t sb_rs, int64_t sb_bs,
                       const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* C, int64_t ldc,
                       int64_t c_gs, int32_t out_dtype, void* stream) {
-    int rc = check_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, sB, sb_rs, sb_bs, M, N, K, C, ldc, out_dtype);
-    if (rc != MX_OK) return rc;
-    if (G < 1 || G > (1 << 20)) return MX_E_SHAPE;
-    if (!offs) return MX_E_NULL;
-    if (!aligned(offs, 4)) return MX_E_ALIGN;
-    const uint64_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
-    const uint64_t slab = matrix_bytes(M, N, ldc, 1);                  // elements of one group's C
-    if (c_gs < int64_t(slab)) return MX_E_STRIDE;
-    const uint64_t tiles = uint64_t(M / 128) * uint64_t(N / 128) * uint64_t(G);
-    if (tiles > 0x7FFFFFFFull) return MX_E_SHAPE;
-    const Span s[6] = {{addr(C), (uint64_t(G - 1) * uint64_t(c_gs) + slab) * esz},
-                       {addr(A), matrix_bytes(M, K, lda, 1)}, {addr(B), matrix_bytes(N, K, ldb, 1)},
-                       {addr(sA), scale_span(M, K / 32, sa_rs, sa_bs)}, {addr(sB), scale_span(N, K / 32, sb_rs, sb_bs)},
-                       {addr(offs), uint64_t(G) * 4}};
-    for (int i = 1; i < 6; ++i)
-        if (overlap(s[0], s[i])) return MX_E_OVERLAP;
-    if (M == 0 || N == 0) return MX_OK;
-    hipError_t e = mxq::launch_mx_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, 0, sB, sb_rs, sb_bs, 0, C, ldc, c_gs, M, N,
-                                       K, offs, G, 1, out_dtype, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+    return gemm_k_call(A, lda, sA, sa_rs, sa_bs, B, ldb, sB, sb_rs, sb_bs, offs, G, M, N, K, C, ldc, c_gs,
+                       out_dtype, false, stream);
+}
+
+int mx_grouped_gemm_k_mfma(const uint8_t* A, int64_t lda, const uint8_t* sA, const uint8_t* B, int64_t ldb,
+                           const uint8_t* sB, const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                           void* C, int64_t ldc, int64_t c_gs, int32_t out_dtype, void* stream) {
+    return gemm_k_call(A, lda, sA, 0, 0, B, ldb, sB, 0, 0, offs, G, M, N, K, C, ldc, c_gs, out_dtype, true, stream);
 }
 
 }  // extern "C"

@@ -15,7 +15,7 @@ namespace mxq {
 hipError_t launch_dual_axis(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x,
                             uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
                             const int32_t* offs, int32_t G, int32_t* err, bool grouped,
-                            hipStream_t stream);
+                            bool mfma_scales, hipStream_t stream);
 
 // Offset validation alone, for a grouped call on an empty matrix.
 hipError_t launch_offs_validate(const int32_t* offs, int32_t G, int64_t M, int32_t* err,
@@ -53,6 +53,7 @@ hipError_t launch_mx9_unpack_records(const uint8_t* packed, int64_t ld_p, int64_
 hipError_t launch_mx_gemm(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, int64_t sa_bs,
                           const uint8_t* B, int64_t ldb, int64_t b_gs, const uint8_t* sB, int64_t sb_rs,
                           int64_t sb_bs, int64_t sb_gs, void* C, int64_t ldc, int64_t c_gs, int64_t M, int64_t N,
-                          int64_t K, const int32_t* offs, int32_t G, int mode, int out_dtype, hipStream_t stream);
+                          int64_t K, const int32_t* offs, int32_t G, int mode, int out_dtype, bool mfma_scales,
+                          hipStream_t stream);
 
 }  // namespace mxq

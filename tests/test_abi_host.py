@@ -25,7 +25,9 @@ def _declared():
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["mx_quantize_2d_dual", "mx_quantize_grouped", "mx9_pack", "mx9_unpack",
                                   "mx9_pack_axis", "mx9_unpack_axis", "mx9_pack_records", "mx9_unpack_records",
-                                  "mx_gemm_nt", "mx_grouped_gemm_rows", "mx_grouped_gemm_k", "mx_status_string"])
+                                  "mx_gemm_nt", "mx_grouped_gemm_rows", "mx_grouped_gemm_k", "mx_status_string",
+                                  "mx_quantize_2d_dual_mfma", "mx_quantize_grouped_mfma", "mx_gemm_nt_mfma",
+                                  "mx_grouped_gemm_rows_mfma", "mx_grouped_gemm_k_mfma"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -164,6 +166,34 @@ def test_gemm_validation_codes():
                                      128, 128, 256, a["C"], 128, cgs, 0, None)
     assert kgroups(G=0) == 5 and kgroups(cgs=128 * 127) == 6
     assert kgroups(C=FAKE * 6 - 4 * 128 * 128 * 2) == 8              # the last group's C runs into offs
+
+
+def test_matrix_core_layout_validation_codes():
+    """The _mfma entry points share the checks of their plain forms, with the
+    scale buffers sized rows * K/32 and required 16-byte aligned."""
+    lib = mxq.library()
+
+    def dual(fn, **kw):
+        a = dict(x=FAKE, M=256, N=256, ld=256, qr=FAKE * 2, sr=FAKE * 3, qc=FAKE * 4, sc=FAKE * 5)
+        a.update(kw)
+        return fn(a["x"], a["M"], a["N"], a["ld"], 32, 0, a["qr"], a["sr"], a["qc"], a["sc"], None)
+    f = lib.mx_quantize_2d_dual_mfma
+    assert dual(f, x=None) == 1 and dual(f, M=200) == 5 and dual(f, ld=128) == 6 and dual(f, sc=FAKE * 5 + 4) == 7
+    assert dual(f, sr=FAKE * 2 + 4096) == 8 and dual(f, M=0, x=None, qr=None, sr=None, qc=None, sc=None) == 0
+    g = lib.mx_quantize_grouped_mfma
+    assert g(FAKE, 256, 256, 256, 32, 0, None, 2, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, None, None) == 1
+    assert g(FAKE, 256, 256, 256, 32, 0, FAKE * 6, -1, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, None, None) == 5
+
+    def gemm(A=FAKE, sA=FAKE * 2, B=FAKE * 3, sB=FAKE * 4, M=128, N=128, K=256, C=FAKE * 5, ldc=128):
+        return lib.mx_gemm_nt_mfma(A, 256, sA, B, 256, sB, M, N, K, C, ldc, 0, None)
+    assert gemm(sA=None) == 1 and gemm(K=96) == 5 and gemm(ldc=64) == 6
+    assert gemm(sA=FAKE * 2 + 4) == 7 and gemm(sB=FAKE * 4 + 8) == 7
+    assert gemm(sB=FAKE * 5 - 128 * 8 + 16) == 8                     # the last scale bytes run into C
+    assert gemm(sB=FAKE * 5 - 128 * 8) != 8
+    assert lib.mx_grouped_gemm_rows_mfma(FAKE, 256, FAKE * 2, FAKE * 3, 256, 1 << 16, FAKE * 4, 1024, None, 4,
+                                         128, 128, 256, FAKE * 5, 128, 0, None) == 1
+    assert lib.mx_grouped_gemm_k_mfma(FAKE, 256, FAKE * 2, FAKE * 3, 256, FAKE * 4, FAKE * 6, 4, 128, 128, 256,
+                                      FAKE * 5, 128, 128 * 127, 0, None) == 6
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch):

@@ -1,0 +1,201 @@
+"""GPU parity of the matrix-core scale layout: the dual-axis cast with
+scale_layout="mfma" (pytorch/ao PR #4995, "[moe_training] Fused dual-axis
+MXFP8 quantization with correct metadata": the kernel writes the consumer's
+swizzled scale layout itself) and the contractions that read it (AMD-AGI/ALTO
+PR #31, "Add MXFP8 grouped GEMM (E4M3) for routed-expert MoE training").
+
+The cast must give the oracle's codes byte for byte and the oracle's scales
+permuted by oracle.scales_to_mfma (s_row as the operand [M rows, N/32
+blocks], s_col transposed to the operand [N rows, M/32 blocks]).  The
+contractions must meet the oracle within the matrix cores' measured bound
+(see test_gpu_gemm.py) and equal the strided-view contraction on the same
+bytes exactly (same instructions, same order).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mx9_dual_axis_amd as mxq
+import oracle
+from helpers import bf16_to_dev, host, require_gpu, say
+from mx9_dual_axis_amd import synth
+from test_gpu_gemm import _assert_close, _codes, _dev
+
+pytestmark = pytest.mark.gpu
+THREADS = 16
+
+
+def _want_mfma(want):
+    """The oracle's dual-axis outputs with both scale tensors in the matrix-core layout."""
+    q_row, s_row, q_col, s_col = want
+    return q_row, oracle.scales_to_mfma(s_row), q_col, oracle.scales_to_mfma(np.ascontiguousarray(s_col.T))
+
+
+def _dirty(M, N, dev, fill=0xA5):
+    kw = dict(dtype=torch.uint8, device=dev)
+    return tuple(torch.full(s, fill, **kw) for s in ((M, N), (M * N // 32,), (N, M), (M * N // 32,)))
+
+
+def _assert_equal(got, want, tag):
+    for name, g, w in zip(("q_row", "s_row", "q_col", "s_col"), got, want):
+        g = host(g)
+        assert g.shape == w.shape, (tag, name, g.shape, w.shape)
+        bad = np.count_nonzero(g != w)
+        if bad:
+            idx = np.argwhere(g != w)[:5]
+            pytest.fail(f"{tag}: {name} differs in {bad} bytes, first at {idx.tolist()}")
+
+
+@pytest.mark.parametrize("M,N,kind,seed", [
+    (128, 128, "special", 1),
+    (256, 384, "normal", 2),
+    (384, 1152, "special", 3),      # N % 512 != 0
+    (640, 2560, "mixed", 4),
+])
+def test_dense_cast_in_the_matrix_core_layout(M, N, kind, seed):
+    dev = require_gpu()
+    say(f"mfma-layout cast M={M} N={N} kind={kind}")
+    xb = {"normal": synth.normal_bf16, "special": synth.special_matrix, "mixed": synth.mixed_rows}[kind](M, N, seed)
+    out = _dirty(M, N, dev)
+    mxq.mx_quantize_2d_dual(bf16_to_dev(xb), out=out, scale_layout="mfma")
+    torch.cuda.synchronize()
+    _assert_equal(out, _want_mfma(oracle.mxfp8_dual(xb, threads=THREADS)), f"{M}x{N}")
+
+
+@pytest.mark.parametrize("offs", [[128, 128, 384, 512], [0, 640], [256, 768, 896]])
+def test_grouped_cast_in_the_matrix_core_layout(offs):
+    dev = require_gpu()
+    M, N = 896, 640
+    say(f"mfma-layout grouped cast M={M} N={N} offs={offs}")
+    xb = synth.special_matrix(M, N, 7)
+    o = np.array(offs, np.int32)
+    err = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    out = _dirty(M, N, dev)
+    mxq.mx_quantize_grouped(bf16_to_dev(xb), _dev(o), err=err, out=out, scale_layout="mfma")
+    torch.cuda.synchronize()
+    rc, want = oracle.mxfp8_grouped(xb, o, threads=THREADS)
+    assert rc == 0 and int(err.item()) == 0
+    _assert_equal(out, _want_mfma(want), f"grouped {offs}")
+
+
+def test_layout_is_a_permutation_of_the_plain_call():
+    """Both layouts of one input on the device: the same multiset of bytes,
+    placed by the oracle's index function."""
+    dev = require_gpu()
+    M, N = 512, 1024
+    say("mfma layout vs plain layout on the device")
+    xd = bf16_to_dev(synth.mixed_rows(M, N, 9))
+    plain = [host(t) for t in mxq.mx_quantize_2d_dual(xd)]
+    mf = [host(t) for t in mxq.mx_quantize_2d_dual(xd, scale_layout="mfma")]
+    torch.cuda.synchronize()
+    assert np.array_equal(mf[0], plain[0]) and np.array_equal(mf[2], plain[2])
+    assert np.array_equal(oracle.scales_from_mfma(mf[1], M, N // 32), plain[1])
+    assert np.array_equal(oracle.scales_from_mfma(mf[3], N, M // 32), plain[3].T)
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (256, 384, 1024)])
+def test_gemm_reads_the_layout(M, N, K):
+    require_gpu()
+    say(f"mx_gemm_nt_mfma [{M}, {N}, {K}]")
+    g = np.random.default_rng(M + 3 * K)
+    A, B = _codes(g, (M, K)), _codes(g, (N, K))
+    sA = g.integers(118, 137, (M, K // 32), dtype=np.uint8)
+    sB = g.integers(118, 137, (N, K // 32), dtype=np.uint8)
+    C = mxq.mx_gemm_nt_mfma(_dev(A), _dev(oracle.scales_to_mfma(sA)), _dev(B), _dev(oracle.scales_to_mfma(sB)))
+    Cs = mxq.mx_gemm_nt(_dev(A), _dev(sA), _dev(B), _dev(sB))
+    torch.cuda.synchronize()
+    ref, absC = oracle.mx_gemm_nt(A, sA, B, sB, sa_strides=(K // 32, 1), sb_strides=(K // 32, 1),
+                                  threads=THREADS, with_abs=True)
+    _assert_close(C, ref, absC, K, torch.float32, "mfma layout")
+    assert torch.equal(C, Cs)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_grouped_gemms_read_the_layout(out_dtype):
+    require_gpu()
+    say(f"grouped contractions, mfma layout -> {out_dtype}")
+    g = np.random.default_rng(11)
+    M, N, K, E = 1024, 256, 384, 5
+    A = _codes(g, (M, K))
+    sA = g.integers(118, 137, (M, K // 32), dtype=np.uint8)
+    B = np.stack([_codes(g, (N, K)) for _ in range(E)])
+    sB = g.integers(118, 137, (E, N, K // 32), dtype=np.uint8)
+    sBm = np.stack([oracle.scales_to_mfma(sB[e]) for e in range(E)])
+    offs = np.array([128, 128, 512, 640, 896], np.int32)
+    C = mxq.mx_grouped_gemm_rows_mfma(_dev(A), _dev(oracle.scales_to_mfma(sA)), _dev(B), _dev(sBm), _dev(offs),
+                                      out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref, absC = oracle.mx_grouped_gemm_rows(A, sA, B, sB, offs, sa_strides=(K // 32, 1), sb_strides=(K // 32, 1),
+                                            threads=THREADS, with_abs=True)
+    _assert_close(C, ref, absC, K, out_dtype, "row groups, mfma layout")
+    assert torch.all(C[offs[-1]:] == 0)
+
+    M2, N2, K2 = 256, 384, 1024
+    A2, B2 = _codes(g, (M2, K2)), _codes(g, (N2, K2))
+    sA2 = g.integers(118, 137, (M2, K2 // 32), dtype=np.uint8)
+    sB2 = g.integers(118, 137, (N2, K2 // 32), dtype=np.uint8)
+    offs2 = np.array([256, 256, 640, 896], np.int32)
+    C2 = mxq.mx_grouped_gemm_k_mfma(_dev(A2), _dev(oracle.scales_to_mfma(sA2)), _dev(B2),
+                                    _dev(oracle.scales_to_mfma(sB2)), _dev(offs2), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref2, abs2 = oracle.mx_grouped_gemm_k(A2, sA2, B2, sB2, offs2, sa_strides=(K2 // 32, 1),
+                                          sb_strides=(K2 // 32, 1), threads=THREADS, with_abs=True)
+    for e in range(4):
+        kk = int(offs2[e] - (offs2[e - 1] if e else 0))
+        _assert_close(C2[e], ref2[e], abs2[e], max(kk, 1), out_dtype, f"contraction group {e}, mfma layout")
+    assert torch.all(C2[1] == 0)
+
+
+def test_grouped_cast_feeds_both_grouped_gemms():
+    """End to end on the device with no rearrangement in between: the grouped
+    cast in the matrix-core layout feeds the row-grouped forward (q_row,
+    s_row) and the contraction-grouped weight gradient (q_col, s_col), and
+    both equal the strided-view path on the plain cast bit for bit and the
+    oracle within the bound."""
+    require_gpu()
+    M, K, N, E = 2048, 512, 256, 6
+    say(f"grouped cast (mfma layout) -> grouped contractions, M={M} K={K} N={N}")
+    xb = synth.normal_bf16(M, K, 31)
+    dyb = synth.normal_bf16(M, N, 32)
+    offs = np.array([256, 256, 768, 1280, 1536, 1920], np.int32)      # an empty group, a 128-row tail
+    od = _dev(offs)
+    xd, dyd = bf16_to_dev(xb), bf16_to_dev(dyb)
+    qx = mxq.mx_quantize_grouped(xd, od, scale_layout="mfma")
+    qd = mxq.mx_quantize_grouped(dyd, od, scale_layout="mfma")
+    px = mxq.mx_quantize_grouped(xd, od)
+    pd = mxq.mx_quantize_grouped(dyd, od)
+    g = np.random.default_rng(12)
+    W = np.stack([_codes(g, (N, K)) for _ in range(E)])
+    sW = g.integers(118, 137, (E, N, K // 32), dtype=np.uint8)
+    sWm = np.stack([oracle.scales_to_mfma(sW[e]) for e in range(E)])
+    Y = mxq.mx_grouped_gemm_rows_mfma(qx[0], qx[1], _dev(W), _dev(sWm), od)
+    Yp = mxq.mx_grouped_gemm_rows(px[0], px[1], _dev(W), _dev(sW), od)
+    dW = mxq.mx_grouped_gemm_k_mfma(qx[2], qx[3], qd[2], qd[3], od)         # [E, K, N]
+    dWp = mxq.mx_grouped_gemm_k(px[2], px[3].t(), pd[2], pd[3].t(), od)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Yp) and torch.equal(dW, dWp)
+    hx = [host(t) for t in px]
+    hd = [host(t) for t in pd]
+    ref, absC = oracle.mx_grouped_gemm_rows(hx[0], hx[1], W, sW, offs, sa_strides=(K // 32, 1),
+                                            sb_strides=(K // 32, 1), threads=THREADS, with_abs=True)
+    _assert_close(Y, ref, absC, K, torch.float32, "forward")
+    ref2, abs2 = oracle.mx_grouped_gemm_k(hx[2], hx[3], hd[2], hd[3], offs, sa_strides=(1, K),
+                                          sb_strides=(1, N), threads=THREADS, with_abs=True)
+    for e in range(E):
+        kk = int(offs[e] - (offs[e - 1] if e else 0))
+        _assert_close(dW[e], ref2[e], abs2[e], max(kk, 1), torch.float32, f"weight gradient group {e}")
+
+
+def test_rejections():
+    dev = require_gpu()
+    say("mfma-layout rejections")
+    a = torch.zeros((128, 128), dtype=torch.uint8, device=dev)
+    s = torch.zeros((512,), dtype=torch.uint8, device=dev)
+    with pytest.raises(ValueError):
+        mxq.mx_gemm_nt_mfma(a, s[:256], a, s)
+    with pytest.raises(mxq.MXError) as ei:
+        big = torch.zeros((520,), dtype=torch.uint8, device=dev)
+        mxq.mx_gemm_nt_mfma(a, big[4:516], a, s)       # scales not 16-byte aligned
+    assert ei.value.status == 7
+    with pytest.raises(ValueError):
+        mxq.mx_quantize_2d_dual(torch.zeros((128, 128), dtype=torch.bfloat16, device=dev), scale_layout="swizzled")

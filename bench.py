@@ -276,26 +276,37 @@ def measure_configs(dev, launches: int, sets: int = 3):
 
 
 PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
 
 
 def measure_gemm(dev, launches: int):
     """The consumer contraction on the matrix cores: the routed-expert forward
     and weight gradient over the grouped activation buffer (its cast outputs,
     64 experts of 2048 output features), and a dense 8192^3 product.  Rates
-    are useful FLOP/s (2 per multiply-add over the covered rows) against the
-    5.0 PFLOP/s dense E4M3 peak."""
+    are useful FLOP/s (2 per multiply-add over the covered rows) and minimal
+    HBM bytes, each workload judged against the roof that binds it: the
+    routed-expert shapes are HBM-bound (each expert's weights serve about 192
+    rows; the weight gradient writes a [5120, 2048] result per group), the
+    dense product is bound by the matrix cores."""
     import numpy as np
     import torch
 
     import mx9_dual_axis_amd as mxq
     from mx9_dual_axis_amd import synth
 
-    def tsum(ts, flops, workload):
+    def tsum(ts, flops, workload, nbytes):
+        """Rates against both roofs; `bound` is the one that limits the
+        workload at peak (time at the roof = the larger of FLOP / 5.0 PFLOP/s
+        and minimal HBM bytes / 8 TB/s), `frac` = that time / measured time."""
         ts = sorted(ts)
         mean = sum(ts) / len(ts)
         tf = flops / mean / 1e12
+        t_mfma = flops / (PEAK_FP8_TFLOPS * 1e12)
+        t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
         return {"workload": workload, "us": round(mean * 1e6, 2), "median_us": round(ts[len(ts) // 2] * 1e6, 2),
-                "flop": int(flops), "TFLOP_s": round(tf, 1), "frac": round(tf / PEAK_FP8_TFLOPS, 4)}
+                "flop": int(flops), "hbm_bytes": int(nbytes), "TFLOP_s": round(tf, 1),
+                "GB_s": round(nbytes / mean / 1e9, 1), "bound": "mfma" if t_mfma >= t_hbm else "hbm",
+                "frac": round(max(t_mfma, t_hbm) / mean, 4)}
 
     print("bench: MXFP8 contractions (grouped forward, weight gradient, dense)", file=sys.stderr, flush=True)
     g = np.random.default_rng(11)
@@ -321,36 +332,46 @@ def measure_gemm(dev, launches: int):
     sW = scales((E, N, K // 32))
     out = torch.empty((Mt, N), dtype=torch.bfloat16, device=dev)
     fwd = [lambda: mxq.mx_grouped_gemm_rows(q_row, s_row, W, sW, od, out=out)]
+    # minimal HBM bytes: covered activation rows and their scales, the weights
+    # and scales of every non-empty expert, the whole bf16 output
+    busy = int(np.count_nonzero(np.diff(np.concatenate([[0], offs])) > 0))
+    fwd_bytes = covered * K * (1 + 1 / 32) + busy * N * K * (1 + 1 / 32) + Mt * N * 2
     res["gemm_grouped_forward"] = tsum(time_rotating(fwd, launches), 2.0 * covered * N * K,
                                        f"grouped forward, cast activations [{Mt}, {K}] (64 groups, {covered} rows) "
-                                       f"x 64 experts [{N}, {K}] -> bf16")
+                                       f"x 64 experts [{N}, {K}] -> bf16", fwd_bytes)
     sWm = sW.reshape(E, N * K // 32)       # random bytes: read as the matrix-core layout
     fwd = [lambda: mxq.mx_grouped_gemm_rows_mfma(m_row, ms_row, W, sWm, od, out=out)]
     res["gemm_grouped_forward_mfma"] = tsum(time_rotating(fwd, launches), 2.0 * covered * N * K,
-                                            "grouped forward as above, scales in the matrix-core layout")
+                                            "grouped forward as above, scales in the matrix-core layout", fwd_bytes)
     del W, sW, sWm, out, fwd
     dY = codes((N, Mt))
     sdY = scales((Mt // 32, N))
     dW = torch.empty((E, K, N), dtype=torch.bfloat16, device=dev)
     wg = [lambda: mxq.mx_grouped_gemm_k(q_col, s_col.t(), dY, sdY.t(), od, out=dW)]
+    # minimal HBM bytes: the covered token columns of both operands with
+    # their scales, and the whole bf16 output of every group
+    wg_bytes = covered * (K + N) * (1 + 1 / 32) + E * K * N * 2
     res["gemm_grouped_wgrad"] = tsum(time_rotating(wg, launches), 2.0 * covered * N * K,
                                      f"grouped weight gradient, cast q_col [{K}, {Mt}] x dY [{N}, {Mt}] over 64 groups "
-                                     f"-> bf16 [64, {K}, {N}]")
+                                     f"-> bf16 [64, {K}, {N}]", wg_bytes)
     sdYm = sdY.reshape(-1)
     wg = [lambda: mxq.mx_grouped_gemm_k_mfma(m_col, ms_col, dY, sdYm, od, out=dW)]
     res["gemm_grouped_wgrad_mfma"] = tsum(time_rotating(wg, launches), 2.0 * covered * N * K,
-                                          "grouped weight gradient as above, scales in the matrix-core layout")
+                                          "grouped weight gradient as above, scales in the matrix-core layout",
+                                          wg_bytes)
     del dY, sdY, sdYm, dW, wg, q_row, s_row, q_col, s_col, m_row, ms_row, m_col, ms_col
     D = 8192
     A, B = codes((D, D)), codes((D, D))
     sA, sB = scales((D, D // 32)), scales((D, D // 32))
     C = torch.empty((D, D), dtype=torch.bfloat16, device=dev)
     dn = [lambda: mxq.mx_gemm_nt(A, sA, B, sB, out=C)]
-    res["gemm_dense_8192"] = tsum(time_rotating(dn, launches), 2.0 * D ** 3, "dense [8192, 8192, 8192] -> bf16")
+    dn_bytes = 2 * D * D * (1 + 1 / 32) + D * D * 2
+    res["gemm_dense_8192"] = tsum(time_rotating(dn, launches), 2.0 * D ** 3, "dense [8192, 8192, 8192] -> bf16",
+                                  dn_bytes)
     sAm, sBm = sA.reshape(-1), sB.reshape(-1)
     dn = [lambda: mxq.mx_gemm_nt_mfma(A, sAm, B, sBm, out=C)]
     res["gemm_dense_8192_mfma"] = tsum(time_rotating(dn, launches), 2.0 * D ** 3,
-                                       "dense [8192, 8192, 8192] -> bf16, scales in the matrix-core layout")
+                                       "dense [8192, 8192, 8192] -> bf16, scales in the matrix-core layout", dn_bytes)
     del A, B, sA, sB, sAm, sBm, C, dn
     torch.cuda.synchronize()
     return res

@@ -41,14 +41,22 @@
 //     group's range of the contraction.
 #include "mxq_kernels.h"
 
+#include <utility>
+
 namespace mxq {
 namespace {
 
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
 
+// s_waitcnt immediate (gfx9 encoding: vmcnt bits 3..0 and 15..14, expcnt
+// 6..4, lgkmcnt 11..8): at most n vector-memory operations outstanding,
+// the other counters not waited on.
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
     const uint8_t* A;
@@ -241,6 +249,259 @@ void mx_gemm_kernel(GemmArgs p) {
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Form for scales in the matrix-core layout (the default consumer path).
+//
+// Same tile and wave decomposition as above (128 x 128, four 64 x 64 wave
+// tiles), with three changes measured on MI355X:
+//   * operands go straight from global memory into LDS (buffer loads with
+//     the LDS destination), so no registers stage them and no LDS write
+//     instructions are issued; the two stages are distinct LDS objects, so
+//     the compiler knows that reading one stage does not wait on the loads
+//     filling the other;
+//   * each lane's scales for a step are one dword per operand;
+//   * the result goes through LDS, 32 rows of a wave tile at a time, and
+//     leaves as full 16-byte pieces of C rows with non-temporal stores (the
+//     weight gradient, whose groups are short, is bound by writing C).
+// Larger tiles (128 x 256 with 64 x 128 wave tiles, or three stages) were
+// slower: one workgroup per CU no longer hides the load latency.
+// ---------------------------------------------------------------------------
+
+// acc[i][J] += a[i] x b for every i (J, the column sub-tile, is fixed).
+template <int J, int MS, int NS, int... I>
+__device__ __forceinline__ void mma_col(v4f (&acc)[MS][NS], const v8i (&a)[MS], const v8i& b, const int (&sa)[MS / 4],
+                                        int sb, std::integer_sequence<int, I...>) {
+    ((acc[I][J] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[I], b, acc[I][J], 0, 0, I & 3, sa[I >> 2], J & 3,
+                                                                   sb)),
+     ...);
+}
+
+// B fragment of column sub-tile J (rows b_row0 + 16 J .. + 15) from LDS.
+template <int J>
+__device__ __forceinline__ v8i b_frag(const uint4* sb_lds, uint32_t b_row0, uint32_t lane) {
+    const uint32_t g = lane >> 4, sw = lane & 7u;
+    const uint32_t r = b_row0 + 16u * J + (lane & 15u);
+    const uint4 lo = sb_lds[r * 8u + (g ^ sw)];
+    const uint4 hi = sb_lds[r * 8u + ((4u + g) ^ sw)];
+    return v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+}
+
+// Column sub-tile J: the next column's B fragment is read from LDS while
+// this column's instructions run (only two B fragments are ever live; the
+// scheduling barriers keep the compiler from hoisting every read of the
+// step, which would not fit the registers).
+template <int J, int MS, int NS>
+__device__ __forceinline__ void mma_b(v4f (&acc)[MS][NS], const v8i (&a)[MS], v8i& b, const uint4* sb_lds,
+                                      uint32_t b_row0, uint32_t lane, const int (&sa)[MS / 4],
+                                      const int (&sb)[NS / 4]) {
+    v8i nb;
+    if constexpr (J + 1 < NS) nb = b_frag<J + 1>(sb_lds, b_row0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_col<J>(acc, a, b, sa, sb[J >> 2], std::make_integer_sequence<int, MS>{});
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (J + 1 < NS) b = nb;
+}
+
+// One 128-wide step from one LDS stage: all A fragments of the wave, then
+// the B fragments one column sub-tile at a time.
+template <int MS, int NS, int... J>
+__device__ __forceinline__ void mma_step(v4f (&acc)[MS][NS], const uint4* sa_lds, const uint4* sb_lds, uint32_t a_row0,
+                                         uint32_t b_row0, uint32_t lane, const int (&sa)[MS / 4],
+                                         const int (&sb)[NS / 4], std::integer_sequence<int, J...>) {
+    const uint32_t g = lane >> 4, sw = lane & 7u;           // a fragment row's index mod 8 is lane % 8
+    v8i a[MS];
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+        const uint32_t r = a_row0 + 16u * i + (lane & 15u);
+        const uint4 lo = sa_lds[r * 8u + (g ^ sw)];
+        const uint4 hi = sa_lds[r * 8u + ((4u + g) ^ sw)];
+        a[i] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+    }
+    v8i b = b_frag<0>(sb_lds, b_row0, lane);
+    (mma_b<J>(acc, a, b, sb_lds, b_row0, lane, sa, sb), ...);
+}
+
+// One stage of operands in LDS: A rows [32 MS][8 chunks], B rows [32 NS][8 chunks].
+template <int MS, int NS>
+struct LdsStage {
+    uint4 a[32 * MS * 8];
+    uint4 b[32 * NS * 8];
+};
+
+// Stages are filled straight from global memory into LDS with buffer loads
+// (16 bytes per lane): lane i of an instruction covering LDS slots [64 j,
+// 64 j + 64) writes slot 64 j + i, i.e. row 8 j + i / 8 at physical chunk
+// i % 8, which holds logical chunk (i % 8) ^ (i / 8) of that row.  Wave w
+// issues the A instructions j = MS w .. MS w + MS - 1 and the B
+// instructions j = NS w .. NS w + NS - 1; rows past a ragged last tile wrap
+// onto valid rows (mask).  The tile's first row is the resource base, the
+// per-lane part of the offset is loop-invariant and the rest (row group,
+// step) is uniform; a tile spans fewer than 256 rows of at most 2^24 bytes,
+// so every offset fits 32 bits.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, int(0xFFFFFFFFu), 0x00020000);
+}
+
+// 16 bytes per lane from the buffer into LDS at lds + 16 * lane (lds is
+// wave-uniform).  The builtin exists only in the device compilation pass.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, uint4* lds, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, int(voff), int(soff),
+                                             0, 0);
+#endif
+}
+
+template <int kOut, int MS, int NS>
+__global__ __launch_bounds__(kThreads, 2)
+void mx_gemm_lds_kernel(GemmArgs p) {
+    constexpr int kTM = 32 * MS, kTN = 32 * NS;
+    constexpr int kEsz = kOut == 0 ? 4 : 2;
+    constexpr int kPitch = 16 * NS * kEsz + 16;                 // staged result row, bytes
+    // two distinct LDS objects, so that reads of one stage need not wait for
+    // the loads still filling the other
+    __shared__ LdsStage<MS, NS> st0, st1;
+
+    const uint32_t t = threadIdx.x, lane = t & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const uint32_t wm = wave >> 1, wn = wave & 1u;
+
+    // ---- which tile, which group, which range of the contraction ----
+    uint32_t tm, tn;
+    int64_t k_lo = 0, k_hi = p.K;
+    const uint8_t* B = p.B;
+    const uint8_t* sB = p.sB;
+    char* C = static_cast<char*>(p.C);
+    bool zero = false;
+    if (p.mode == 0) {
+        tm = blockIdx.x % p.tiles_m;
+        tn = blockIdx.x / p.tiles_m;
+        if (p.offs != nullptr) {                                // kTM == 128: one group unit
+            const int64_t row = int64_t(tm) * kTM;
+            int32_t g = 0;
+            while (g < p.G && int64_t(p.offs[g]) <= row) ++g;
+            if (g == p.G) {
+                zero = true;
+            } else {
+                B += int64_t(g) * p.b_gs;
+                sB += int64_t(g) * p.sb_gs;
+            }
+        }
+    } else {
+        const uint32_t per = p.tiles_m * p.tiles_n;
+        const uint32_t g = blockIdx.x / per, r = blockIdx.x - g * per;
+        tm = r % p.tiles_m;
+        tn = r / p.tiles_m;
+        k_lo = g == 0 ? 0 : clamp_end(p.offs[g - 1], 0, p.K);
+        k_hi = clamp_end(p.offs[g], k_lo, p.K);
+        C += int64_t(g) * p.c_gs * kEsz;
+    }
+    const int64_t m0 = int64_t(tm) * kTM, n0 = int64_t(tn) * kTN;
+
+    v4f acc[MS][NS];
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // M and N are multiples of 128, so a tile holds 128 or 256 valid rows
+    const uint32_t a_mask = uint32_t(min(int64_t(kTM), p.M - m0)) - 1u;
+    const uint32_t b_mask = uint32_t(min(int64_t(kTN), p.N - n0)) - 1u;
+    const uint32_t lda = uint32_t(p.lda), ldb = uint32_t(p.ldb);              // at most 2^24
+    const uint32_t lr = lane >> 3, lc = (lane & 7u) ^ (lane >> 3);
+    const uint32_t voa = lr * lda + 16u * lc, vob = lr * ldb + 16u * lc;
+    const __amdgpu_buffer_rsrc_t ra = tile_rsrc(p.A + m0 * p.lda);
+    const __amdgpu_buffer_rsrc_t rb = tile_rsrc(B + n0 * p.ldb);
+    // scales: one dword per lane and 64-row group of the wave tile
+    const int64_t ga0 = min((m0 + wm * 16 * MS) / 64, p.M / 64 - MS / 4);
+    const int64_t gb0 = min((n0 + wn * 16 * NS) / 64, p.N / 64 - NS / 4);
+    const uint8_t* sa_w = p.sA + ga0 * p.sa_rs;
+    const uint8_t* sb_w = sB + gb0 * p.sb_rs;
+    const uint32_t so_lane = 4u * lane;
+    const int64_t n = zero ? 0 : (k_hi - k_lo) / kTile;          // steps (none for a tail tile)
+
+    int sa0[MS / 4], sb0[NS / 4], sa1[MS / 4], sb1[NS / 4];
+#define MXQ_FILL(ST, SA, SB, step)                                                               \
+    do {                                                                                         \
+        const int64_t k_ = k_lo + int64_t(step) * kTile;                                         \
+        _Pragma("unroll") for (int q_ = 0; q_ < MS; ++q_) {                                     \
+            const uint32_t j_ = wave * MS + q_;                                                  \
+            buffer_load_lds16(ra, &ST.a[64 * j_], voa, ((8u * j_) & a_mask) * lda + uint32_t(k_)); \
+        }                                                                                        \
+        _Pragma("unroll") for (int q_ = 0; q_ < NS; ++q_) {                                     \
+            const uint32_t j_ = wave * NS + q_;                                                  \
+            buffer_load_lds16(rb, &ST.b[64 * j_], vob, ((8u * j_) & b_mask) * ldb + uint32_t(k_)); \
+        }                                                                                        \
+        _Pragma("unroll") for (int j_ = 0; j_ < MS / 4; ++j_)                                    \
+            SA[j_] = *reinterpret_cast<const int*>(sa_w + (j_ * p.sa_rs + (k_ / kTile) * 256) + so_lane); \
+        _Pragma("unroll") for (int j_ = 0; j_ < NS / 4; ++j_)                                    \
+            SB[j_] = *reinterpret_cast<const int*>(sb_w + (j_ * p.sb_rs + (k_ / kTile) * 256) + so_lane); \
+    } while (0)
+    // step s: its loads (issued one step earlier) complete in every wave,
+    // then the next step's loads go into the other stage while this one is
+    // computed
+#define MXQ_STEP(CUR, NXT, SAC, SBC, SAN, SBN, step)                                             \
+    do {                                                                                         \
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));                                                \
+        __syncthreads();                                                                         \
+        if ((step) + 1 < n) MXQ_FILL(NXT, SAN, SBN, (step) + 1);                                 \
+        mma_step<MS, NS>(acc, CUR.a, CUR.b, wm * 16u * MS, wn * 16u * NS, lane, SAC, SBC,        \
+                         std::make_integer_sequence<int, NS>{});                                 \
+    } while (0)
+
+    if (n > 0) MXQ_FILL(st0, sa0, sb0, 0);
+    int64_t s = 0;
+    for (; s + 2 <= n; s += 2) {
+        MXQ_STEP(st0, st1, sa0, sb0, sa1, sb1, s);
+        MXQ_STEP(st1, st0, sa1, sb1, sa0, sb0, s + 1);
+    }
+    if (s < n) MXQ_STEP(st0, st1, sa0, sb0, sa1, sb1, s);
+#undef MXQ_STEP
+#undef MXQ_FILL
+    __syncthreads();
+
+    // ---- epilogue through LDS: 32 rows of the wave tile at a time ----
+    // acc[i][j][v] is C[m0 + 16 MS wm + 16 i + 4 (lane / 16) + v][n0 + 16 NS wn + 16 j + lane % 16];
+    // wave w stages in its own half of a stage
+    constexpr int kHalf = int(sizeof(LdsStage<MS, NS>)) / 2;
+    static_assert(32 * kPitch <= kHalf, "epilogue chunk must fit half a stage");
+    uint8_t* ep = reinterpret_cast<uint8_t*>(wave < 2 ? &st0 : &st1) + (wave & 1u) * kHalf;
+    constexpr int kPieces = 16 * NS * kEsz / 16;               // 16-byte pieces per staged row
+#pragma unroll
+    for (int h = 0; h < MS / 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint32_t row = 16u * i + 4u * (lane >> 4) + v, col = 16u * j + (lane & 15u);
+                    const float x = acc[2 * h + i][j][v];
+                    if (kOut == 0) *reinterpret_cast<float*>(ep + row * kPitch + col * 4u) = x;
+                    else *reinterpret_cast<__bf16*>(ep + row * kPitch + col * 2u) = __bf16(x);
+                }
+                __builtin_amdgcn_sched_barrier(0);             // one sub-tile's values live at a time
+            }
+        __builtin_amdgcn_s_waitcnt(0xC07F);                     // lgkmcnt(0): this wave's staging writes done
+        __builtin_amdgcn_wave_barrier();
+        const int64_t row0 = m0 + 16 * MS * wm + 32 * h;
+        const int64_t col0 = n0 + 16 * NS * wn;
+#pragma unroll
+        for (int q = 0; q < 32 * kPieces / 64; ++q) {
+            const uint32_t piece = 64u * q + lane;
+            const uint32_t row = piece / kPieces, pc = piece % kPieces;
+            const int64_t grow = row0 + row, gcol = col0 + pc * (16 / kEsz);
+            const uint4 val = *reinterpret_cast<const uint4*>(ep + row * kPitch + 16u * pc);
+            if (grow < p.M && gcol < p.N) {
+                const u32x4 vv = {val.x, val.y, val.z, val.w};
+                __builtin_nontemporal_store(vv, reinterpret_cast<u32x4*>(C + (grow * p.ldc + gcol) * kEsz));
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);                     // reads done before the next chunk's writes
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 }  // namespace
 
 hipError_t launch_mx_gemm(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, int64_t sa_bs,
@@ -257,6 +518,19 @@ hipError_t launch_mx_gemm(const uint8_t* A, int64_t lda, const uint8_t* sA, int6
         // the K/32 scale bytes of each of 64 rows
         p.sa_rs = p.sb_rs = 2 * K;
         p.sa_bs = p.sb_bs = 0;
+    }
+    // the matrix-core-layout form stores 16-byte pieces of C rows
+    const int64_t esz = out_dtype == 0 ? 4 : 2;
+    const bool rows16 = (reinterpret_cast<uintptr_t>(C) % 16 == 0) && (ldc * esz) % 16 == 0 &&
+                        (mode != 1 || (c_gs * esz) % 16 == 0);
+    if (mfma_scales && rows16) {
+        p.tiles_m = uint32_t(M / kTile);
+        p.tiles_n = uint32_t(N / kTile);
+        const uint32_t tiles = p.tiles_m * p.tiles_n * uint32_t(mode == 1 ? G : 1);
+        const dim3 grid(tiles), block(kThreads);
+        if (out_dtype == 0) hipLaunchKernelGGL((mx_gemm_lds_kernel<0, 4, 4>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((mx_gemm_lds_kernel<1, 4, 4>), grid, block, 0, stream, p);
+        return hipGetLastError();
     }
     p.tiles_m = uint32_t(M / kTile);
     p.tiles_n = uint32_t(N / kTile);

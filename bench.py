@@ -509,7 +509,7 @@ def main():
                    "step_algorithmic_bytes": int(step_bytes)},
         "roofline": {"bound": "hbm", "achieved": dual["GB_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(dual["GB_s"] / PEAK_HBM_GBS, 4), "traffic": committed_traffic(),
-                     "kernel": "dual_axis_kernel<false,true> + srow_permute_kernel (one dual-axis call)",
+                     "kernel": "dual_axis_kernel<false, 1> + srow_permute_kernel (one dual-axis call)",
                      "algorithmic_bytes_per_launch": dual["bytes"],
                      "avg_launch_us": dual["us"]},
         "kernels": kernels,

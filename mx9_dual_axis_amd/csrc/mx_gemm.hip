@@ -49,10 +49,6 @@ namespace {
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
 
-// s_waitcnt immediate (gfx9 encoding: vmcnt bits 3..0 and 15..14, expcnt
-// 6..4, lgkmcnt 11..8): at most n vector-memory operations outstanding,
-// the other counters not waited on.
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -250,24 +246,6 @@ void mx_gemm_kernel(GemmArgs p) {
 }
 
 
-// ---------------------------------------------------------------------------
-// Form for scales in the matrix-core layout (the default consumer path).
-//
-// Same tile and wave decomposition as above (128 x 128, four 64 x 64 wave
-// tiles), with three changes measured on MI355X:
-//   * operands go straight from global memory into LDS (buffer loads with
-//     the LDS destination), so no registers stage them and no LDS write
-//     instructions are issued; the two stages are distinct LDS objects, so
-//     the compiler knows that reading one stage does not wait on the loads
-//     filling the other;
-//   * each lane's scales for a step are one dword per operand;
-//   * the result goes through LDS, 32 rows of a wave tile at a time, and
-//     leaves as full 16-byte pieces of C rows with non-temporal stores (the
-//     weight gradient, whose groups are short, is bound by writing C).
-// Larger tiles (128 x 256 with 64 x 128 wave tiles, or three stages) were
-// slower: one workgroup per CU no longer hides the load latency.
-// ---------------------------------------------------------------------------
-
 // acc[i][J] += a[i] x b for every i (J, the column sub-tile, is fixed).
 template <int J, int MS, int NS, int... I>
 __device__ __forceinline__ void mma_col(v4f (&acc)[MS][NS], const v8i (&a)[MS], const v8i& b, const int (&sa)[MS / 4],
@@ -322,49 +300,92 @@ __device__ __forceinline__ void mma_step(v4f (&acc)[MS][NS], const uint4* sa_lds
     (mma_b<J>(acc, a, b, sb_lds, b_row0, lane, sa, sb), ...);
 }
 
-// One stage of operands in LDS: A rows [32 MS][8 chunks], B rows [32 NS][8 chunks].
-template <int MS, int NS>
-struct LdsStage {
-    uint4 a[32 * MS * 8];
-    uint4 b[32 * NS * 8];
+// ---------------------------------------------------------------------------
+// Form for scales in the matrix-core layout (the default consumer path).
+//
+// Measured on MI355X, the first kernel is bound by LDS throughput: a 64 x 64
+// wave tile reads 16 KB of fragments per 16 instructions.  Counters showed
+// the LDS data FIFO full 58% of cycles, no bank conflicts and the matrix
+// cores busy 30%.  This form changes four things:
+//   * wave tiles of 64 x (16 NS): NS = 8 (64 x 128, a 256 x 256 tile of 8
+//     waves, 2 per SIMD) reads a quarter fewer LDS bytes per instruction;
+//     row groups use NS = 4 (128 x 256 tiles, since a group unit is 128 rows);
+//   * operands and the step's scale dwords go straight from global memory
+//     into LDS (buffer loads with the LDS destination); no registers stage
+//     them and no LDS writes are issued;
+//   * those loads and the workgroup barrier are written as instructions with
+//     explicit waits.  The compiler's barrier waits for every outstanding
+//     load, which would limit the pipeline to one step ahead; loads complete
+//     in issue order, so at step s a wave waits until only the later steps'
+//     loads are outstanding.  With three stages (NS = 4) loads run two steps
+//     ahead; the 256 x 256 tile fits two stages;
+//   * the result goes through LDS and leaves as full 16-byte pieces of C
+//     rows with non-temporal stores (the weight gradient, whose groups are
+//     short, is bound by writing C).
+// Each wave issues the same number of loads per step (its A and B pieces
+// and one scale run; waves past the runs repeat the last into a spare slot),
+// which is what the waits count.
+// ---------------------------------------------------------------------------
+
+constexpr int kPipeThreads = 512;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Buffer resource for base (uniform): raw, 4 GiB range.
+__device__ __forceinline__ v4i pipe_rsrc(const uint8_t* base) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    v4i r;
+    r.x = __builtin_amdgcn_readfirstlane(int(uint32_t(b)));
+    r.y = __builtin_amdgcn_readfirstlane(int(uint32_t(b >> 32)));
+    r.z = -1;
+    r.w = 0x00020000;
+    return r;
+}
+
+// 16 (or 4) bytes per lane from the buffer at voff + soff into LDS at
+// lds + 16 (or 4) * lane; lds and soff are uniform.
+__device__ __forceinline__ void pipe_load16(v4i r, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(lds)
+                 : "memory");
+}
+__device__ __forceinline__ void pipe_load4(v4i r, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(lds)
+                 : "memory");
+}
+
+// Wait until at most kOut loads are outstanding and this wave's LDS reads
+// are done, then synchronize the workgroup.
+template <int kLeft>
+__device__ __forceinline__ void pipe_sync() {
+    static_assert(kLeft >= 0 && kLeft < 16, "vmcnt immediate");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kLeft) : "memory");
+}
+
+// Configuration: WM x WN waves of 64 x 16 NS each; the tile is 64 WM x 16 NS WN.
+template <int WM, int NS>
+struct Pipe {
+    static constexpr int WN = 8 / WM;
+    static constexpr int kTM = 64 * WM, kTN = 16 * NS * WN;
+    static constexpr uint32_t kA = 0, kB = uint32_t(kTM) * 128, kS = kB + uint32_t(kTN) * 128;
+    static constexpr uint32_t kStage = kS + 8 * 256;            // + 8 scale runs of 256 bytes
+    static constexpr int kStages = (160 * 1024) / kStage >= 3 ? 3 : 2;
+    static constexpr int kLA = WM, kLB = NS * WN / 4;            // 16-byte loads per wave and step
+    static constexpr int kRunsA = WM, kRuns = WM + NS * WN / 4;  // scale runs (A groups, then B groups)
+    static constexpr int kLoads = kLA + kLB + 1;
 };
 
-// Stages are filled straight from global memory into LDS with buffer loads
-// (16 bytes per lane): lane i of an instruction covering LDS slots [64 j,
-// 64 j + 64) writes slot 64 j + i, i.e. row 8 j + i / 8 at physical chunk
-// i % 8, which holds logical chunk (i % 8) ^ (i / 8) of that row.  Wave w
-// issues the A instructions j = MS w .. MS w + MS - 1 and the B
-// instructions j = NS w .. NS w + NS - 1; rows past a ragged last tile wrap
-// onto valid rows (mask).  The tile's first row is the resource base, the
-// per-lane part of the offset is loop-invariant and the rest (row group,
-// step) is uniform; a tile spans fewer than 256 rows of at most 2^24 bytes,
-// so every offset fits 32 bits.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, int(0xFFFFFFFFu), 0x00020000);
-}
-
-// 16 bytes per lane from the buffer into LDS at lds + 16 * lane (lds is
-// wave-uniform).  The builtin exists only in the device compilation pass.
-__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, uint4* lds, uint32_t voff, uint32_t soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, int(voff), int(soff),
-                                             0, 0);
-#endif
-}
-
-template <int kOut, int MS, int NS>
-__global__ __launch_bounds__(kThreads, 2)
-void mx_gemm_lds_kernel(GemmArgs p) {
-    constexpr int kTM = 32 * MS, kTN = 32 * NS;
+template <int kOut, int WM, int NS>
+__global__ __launch_bounds__(kPipeThreads)
+void mx_gemm_pipe_kernel(GemmArgs p) {
+    using P = Pipe<WM, NS>;
     constexpr int kEsz = kOut == 0 ? 4 : 2;
     constexpr int kPitch = 16 * NS * kEsz + 16;                 // staged result row, bytes
-    // two distinct LDS objects, so that reads of one stage need not wait for
-    // the loads still filling the other
-    __shared__ LdsStage<MS, NS> st0, st1;
+    static_assert(P::kRuns <= 8, "one scale run per wave");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[P::kStages * P::kStage];
 
     const uint32_t t = threadIdx.x, lane = t & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const uint32_t wm = wave >> 1, wn = wave & 1u;
+    const uint32_t wm = wave / P::WN, wn = wave % P::WN;
 
     // ---- which tile, which group, which range of the contraction ----
     uint32_t tm, tn;
@@ -377,7 +398,7 @@ void mx_gemm_lds_kernel(GemmArgs p) {
         tm = blockIdx.x % p.tiles_m;
         tn = blockIdx.x / p.tiles_m;
         if (p.offs != nullptr) {                                // kTM == 128: one group unit
-            const int64_t row = int64_t(tm) * kTM;
+            const int64_t row = int64_t(tm) * P::kTM;
             int32_t g = 0;
             while (g < p.G && int64_t(p.offs[g]) <= row) ++g;
             if (g == p.G) {
@@ -396,98 +417,94 @@ void mx_gemm_lds_kernel(GemmArgs p) {
         k_hi = clamp_end(p.offs[g], k_lo, p.K);
         C += int64_t(g) * p.c_gs * kEsz;
     }
-    const int64_t m0 = int64_t(tm) * kTM, n0 = int64_t(tn) * kTN;
+    const int64_t m0 = int64_t(tm) * P::kTM, n0 = int64_t(tn) * P::kTN;
+    const int64_t n = zero ? 0 : (k_hi - k_lo) / kTile;
 
-    v4f acc[MS][NS];
+    // ---- load plan (all offsets fit 32 bits: a tile spans <= 256 rows of <= 2^24 bytes) ----
+    const uint32_t lda = uint32_t(p.lda), ldb = uint32_t(p.ldb);
+    const uint32_t lr = lane >> 3, lc = (lane & 7u) ^ (lane >> 3);
+    const uint32_t voa = lr * lda + 16u * lc, vob = lr * ldb + 16u * lc;
+    // M and N are multiples of 128: rows past a ragged last tile wrap onto valid rows
+    const uint32_t a_mask = uint32_t(min(int64_t(P::kTM), p.M - m0)) - 1u;
+    const uint32_t b_mask = uint32_t(min(int64_t(P::kTN), p.N - n0)) - 1u;
+    const v4i ra = pipe_rsrc(p.A + m0 * p.lda);
+    const v4i rb = pipe_rsrc(B + n0 * p.ldb);
+    // scale run of this wave (A groups first, then B groups; groups past a
+    // ragged last tile clamp to the last one; waves past the runs repeat the last)
+    const uint32_t run = wave < uint32_t(P::kRuns) ? wave : uint32_t(P::kRuns - 1);
+    const int64_t ga_max = p.M / 64 - 1 - m0 / 64, gb_max = p.N / 64 - 1 - n0 / 64;
+    const v4i rs_a = pipe_rsrc(p.sA + (m0 / 64) * p.sa_rs);
+    const v4i rs_b = pipe_rsrc(sB + (n0 / 64) * p.sb_rs);
+    const bool run_a = run < uint32_t(P::kRunsA);
+    const uint32_t s_run_off = run_a ? uint32_t(min(int64_t(run), ga_max)) * uint32_t(p.sa_rs)
+                                     : uint32_t(min(int64_t(run - P::kRunsA), gb_max)) * uint32_t(p.sb_rs);
+    const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(lds));
+#define MXQ_PIPE_ISSUE(step)                                                                     \
+    do {                                                                                         \
+        const uint32_t k_ = uint32_t(k_lo + int64_t(step) * kTile);                              \
+        const uint32_t st_ = lds0 + uint32_t((step) % P::kStages) * P::kStage;                   \
+        _Pragma("unroll") for (int q_ = 0; q_ < P::kLA; ++q_) {                                  \
+            const uint32_t j_ = uint32_t(P::kLA) * wave + q_;                                    \
+            pipe_load16(ra, st_ + P::kA + 1024u * j_, voa, ((8u * j_) & a_mask) * lda + k_);     \
+        }                                                                                        \
+        _Pragma("unroll") for (int q_ = 0; q_ < P::kLB; ++q_) {                                  \
+            const uint32_t j_ = uint32_t(P::kLB) * wave + q_;                                    \
+            pipe_load16(rb, st_ + P::kB + 1024u * j_, vob, ((8u * j_) & b_mask) * ldb + k_);     \
+        }                                                                                        \
+        pipe_load4(run_a ? rs_a : rs_b, st_ + P::kS + 256u * wave, 4u * lane,                    \
+                   s_run_off + (k_ / uint32_t(kTile)) * 256u);                                   \
+    } while (0)
+
+    v4f acc[4][NS];
 #pragma unroll
-    for (int i = 0; i < MS; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < NS; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // M and N are multiples of 128, so a tile holds 128 or 256 valid rows
-    const uint32_t a_mask = uint32_t(min(int64_t(kTM), p.M - m0)) - 1u;
-    const uint32_t b_mask = uint32_t(min(int64_t(kTN), p.N - n0)) - 1u;
-    const uint32_t lda = uint32_t(p.lda), ldb = uint32_t(p.ldb);              // at most 2^24
-    const uint32_t lr = lane >> 3, lc = (lane & 7u) ^ (lane >> 3);
-    const uint32_t voa = lr * lda + 16u * lc, vob = lr * ldb + 16u * lc;
-    const __amdgpu_buffer_rsrc_t ra = tile_rsrc(p.A + m0 * p.lda);
-    const __amdgpu_buffer_rsrc_t rb = tile_rsrc(B + n0 * p.ldb);
-    // scales: one dword per lane and 64-row group of the wave tile
-    const int64_t ga0 = min((m0 + wm * 16 * MS) / 64, p.M / 64 - MS / 4);
-    const int64_t gb0 = min((n0 + wn * 16 * NS) / 64, p.N / 64 - NS / 4);
-    const uint8_t* sa_w = p.sA + ga0 * p.sa_rs;
-    const uint8_t* sb_w = sB + gb0 * p.sb_rs;
-    const uint32_t so_lane = 4u * lane;
-    const int64_t n = zero ? 0 : (k_hi - k_lo) / kTile;          // steps (none for a tail tile)
-
-    int sa0[MS / 4], sb0[NS / 4], sa1[MS / 4], sb1[NS / 4];
-#define MXQ_FILL(ST, SA, SB, step)                                                               \
-    do {                                                                                         \
-        const int64_t k_ = k_lo + int64_t(step) * kTile;                                         \
-        _Pragma("unroll") for (int q_ = 0; q_ < MS; ++q_) {                                     \
-            const uint32_t j_ = wave * MS + q_;                                                  \
-            buffer_load_lds16(ra, &ST.a[64 * j_], voa, ((8u * j_) & a_mask) * lda + uint32_t(k_)); \
-        }                                                                                        \
-        _Pragma("unroll") for (int q_ = 0; q_ < NS; ++q_) {                                     \
-            const uint32_t j_ = wave * NS + q_;                                                  \
-            buffer_load_lds16(rb, &ST.b[64 * j_], vob, ((8u * j_) & b_mask) * ldb + uint32_t(k_)); \
-        }                                                                                        \
-        _Pragma("unroll") for (int j_ = 0; j_ < MS / 4; ++j_)                                    \
-            SA[j_] = *reinterpret_cast<const int*>(sa_w + (j_ * p.sa_rs + (k_ / kTile) * 256) + so_lane); \
-        _Pragma("unroll") for (int j_ = 0; j_ < NS / 4; ++j_)                                    \
-            SB[j_] = *reinterpret_cast<const int*>(sb_w + (j_ * p.sb_rs + (k_ / kTile) * 256) + so_lane); \
-    } while (0)
-    // step s: its loads (issued one step earlier) complete in every wave,
-    // then the next step's loads go into the other stage while this one is
-    // computed
-#define MXQ_STEP(CUR, NXT, SAC, SBC, SAN, SBN, step)                                             \
-    do {                                                                                         \
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));                                                \
-        __syncthreads();                                                                         \
-        if ((step) + 1 < n) MXQ_FILL(NXT, SAN, SBN, (step) + 1);                                 \
-        mma_step<MS, NS>(acc, CUR.a, CUR.b, wm * 16u * MS, wn * 16u * NS, lane, SAC, SBC,        \
-                         std::make_integer_sequence<int, NS>{});                                 \
-    } while (0)
-
-    if (n > 0) MXQ_FILL(st0, sa0, sb0, 0);
-    int64_t s = 0;
-    for (; s + 2 <= n; s += 2) {
-        MXQ_STEP(st0, st1, sa0, sb0, sa1, sb1, s);
-        MXQ_STEP(st1, st0, sa1, sb1, sa0, sb0, s + 1);
+#pragma unroll
+    for (int s0 = 0; s0 < P::kStages - 1; ++s0)
+        if (s0 < n) MXQ_PIPE_ISSUE(s0);
+    for (int64_t s = 0; s < n; ++s) {
+        // step s's loads are in LDS (the later issued steps may still be in
+        // flight) and the stage step s - 1 used is free
+        if (P::kStages == 3 && s + 1 < n) pipe_sync<P::kLoads>();
+        else pipe_sync<0>();
+        if (s + P::kStages - 1 < n) MXQ_PIPE_ISSUE(s + P::kStages - 1);
+        const uint8_t* st = lds + uint32_t(s % P::kStages) * P::kStage;
+        int sa[1], sb[NS / 4];
+        sa[0] = *reinterpret_cast<const int*>(st + P::kS + 256u * wm + 4u * lane);
+#pragma unroll
+        for (int j = 0; j < NS / 4; ++j)
+            sb[j] = *reinterpret_cast<const int*>(st + P::kS + 256u * (P::kRunsA + (NS / 4) * wn + j) + 4u * lane);
+        mma_step<4, NS>(acc, reinterpret_cast<const uint4*>(st + P::kA), reinterpret_cast<const uint4*>(st + P::kB),
+                        wm * 64u, wn * 16u * NS, lane, sa, sb, std::make_integer_sequence<int, NS>{});
     }
-    if (s < n) MXQ_STEP(st0, st1, sa0, sb0, sa1, sb1, s);
-#undef MXQ_STEP
-#undef MXQ_FILL
+#undef MXQ_PIPE_ISSUE
     __syncthreads();
 
-    // ---- epilogue through LDS: 32 rows of the wave tile at a time ----
-    // acc[i][j][v] is C[m0 + 16 MS wm + 16 i + 4 (lane / 16) + v][n0 + 16 NS wn + 16 j + lane % 16];
-    // wave w stages in its own half of a stage
-    constexpr int kHalf = int(sizeof(LdsStage<MS, NS>)) / 2;
-    static_assert(32 * kPitch <= kHalf, "epilogue chunk must fit half a stage");
-    uint8_t* ep = reinterpret_cast<uint8_t*>(wave < 2 ? &st0 : &st1) + (wave & 1u) * kHalf;
+    // ---- epilogue through LDS: 16 rows of the wave tile at a time, 16-byte non-temporal stores ----
+    // acc[i][j][v] is C[m0 + 64 wm + 16 i + 4 (lane / 16) + v][n0 + 16 NS wn + 16 j + lane % 16]
+    uint8_t* ep = lds + wave * (16 * kPitch);
     constexpr int kPieces = 16 * NS * kEsz / 16;               // 16-byte pieces per staged row
 #pragma unroll
-    for (int h = 0; h < MS / 2; ++h) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < NS; ++j) {
 #pragma unroll
-            for (int j = 0; j < NS; ++j) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const uint32_t row = 16u * i + 4u * (lane >> 4) + v, col = 16u * j + (lane & 15u);
-                    const float x = acc[2 * h + i][j][v];
-                    if (kOut == 0) *reinterpret_cast<float*>(ep + row * kPitch + col * 4u) = x;
-                    else *reinterpret_cast<__bf16*>(ep + row * kPitch + col * 2u) = __bf16(x);
-                }
-                __builtin_amdgcn_sched_barrier(0);             // one sub-tile's values live at a time
+            for (int v = 0; v < 4; ++v) {
+                const uint32_t row = 4u * (lane >> 4) + v, col = 16u * j + (lane & 15u);
+                const float x = acc[i][j][v];
+                if (kOut == 0) *reinterpret_cast<float*>(ep + row * kPitch + col * 4u) = x;
+                else *reinterpret_cast<__bf16*>(ep + row * kPitch + col * 2u) = __bf16(x);
             }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         __builtin_amdgcn_s_waitcnt(0xC07F);                     // lgkmcnt(0): this wave's staging writes done
         __builtin_amdgcn_wave_barrier();
-        const int64_t row0 = m0 + 16 * MS * wm + 32 * h;
+        const int64_t row0 = m0 + 64 * wm + 16 * i;
         const int64_t col0 = n0 + 16 * NS * wn;
 #pragma unroll
-        for (int q = 0; q < 32 * kPieces / 64; ++q) {
+        for (int q = 0; q < 16 * kPieces / 64; ++q) {
             const uint32_t piece = 64u * q + lane;
             const uint32_t row = piece / kPieces, pc = piece % kPieces;
             const int64_t grow = row0 + row, gcol = col0 + pc * (16 / kEsz);
@@ -524,12 +541,23 @@ hipError_t launch_mx_gemm(const uint8_t* A, int64_t lda, const uint8_t* sA, int6
     const bool rows16 = (reinterpret_cast<uintptr_t>(C) % 16 == 0) && (ldc * esz) % 16 == 0 &&
                         (mode != 1 || (c_gs * esz) % 16 == 0);
     if (mfma_scales && rows16) {
-        p.tiles_m = uint32_t(M / kTile);
-        p.tiles_n = uint32_t(N / kTile);
-        const uint32_t tiles = p.tiles_m * p.tiles_n * uint32_t(mode == 1 ? G : 1);
-        const dim3 grid(tiles), block(kThreads);
-        if (out_dtype == 0) hipLaunchKernelGGL((mx_gemm_lds_kernel<0, 4, 4>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((mx_gemm_lds_kernel<1, 4, 4>), grid, block, 0, stream, p);
+        // row groups: 128-row tiles (one group unit); otherwise 256 x 256
+        const bool row_groups = mode == 0 && offs != nullptr;
+        if (row_groups) {
+            using P = Pipe<2, 4>;
+            p.tiles_m = uint32_t(M / P::kTM);
+            p.tiles_n = uint32_t((N + P::kTN - 1) / P::kTN);
+            const dim3 grid(p.tiles_m * p.tiles_n), block(kPipeThreads);
+            if (out_dtype == 0) hipLaunchKernelGGL((mx_gemm_pipe_kernel<0, 2, 4>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((mx_gemm_pipe_kernel<1, 2, 4>), grid, block, 0, stream, p);
+        } else {
+            using P = Pipe<4, 8>;
+            p.tiles_m = uint32_t((M + P::kTM - 1) / P::kTM);
+            p.tiles_n = uint32_t((N + P::kTN - 1) / P::kTN);
+            const dim3 grid(p.tiles_m * p.tiles_n * uint32_t(mode == 1 ? G : 1)), block(kPipeThreads);
+            if (out_dtype == 0) hipLaunchKernelGGL((mx_gemm_pipe_kernel<0, 4, 8>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((mx_gemm_pipe_kernel<1, 4, 8>), grid, block, 0, stream, p);
+        }
         return hipGetLastError();
     }
     p.tiles_m = uint32_t(M / kTile);

@@ -19,7 +19,7 @@ import mx9_dual_axis_amd as mxq
 import oracle
 from helpers import bf16_to_dev, host, require_gpu, say
 from mx9_dual_axis_amd import synth
-from test_gpu_gemm import _assert_close, _codes, _dev
+from test_gpu_gemm import DEV, _assert_close, _codes, _dev
 
 pytestmark = pytest.mark.gpu
 THREADS = 16
@@ -184,6 +184,59 @@ def test_grouped_cast_feeds_both_grouped_gemms():
     for e in range(E):
         kk = int(offs[e] - (offs[e - 1] if e else 0))
         _assert_close(dW[e], ref2[e], abs2[e], max(kk, 1), torch.float32, f"weight gradient group {e}")
+
+
+def test_unaligned_output_rows_take_the_strided_kernel():
+    """An output pitch that leaves C rows off 16-byte boundaries cannot take
+    the 16-byte stores of the pipelined form; the first kernel reads the
+    matrix-core layout then.  Same results as the aligned call."""
+    require_gpu()
+    say("mx_gemm_nt_mfma with an odd output pitch")
+    g = np.random.default_rng(13)
+    M, N, K = 256, 384, 512
+    A, B = _codes(g, (M, K)), _codes(g, (N, K))
+    sA = g.integers(118, 137, (M, K // 32), dtype=np.uint8)
+    sB = g.integers(118, 137, (N, K // 32), dtype=np.uint8)
+    dA, dB = _dev(A), _dev(B)
+    msA, msB = _dev(oracle.scales_to_mfma(sA)), _dev(oracle.scales_to_mfma(sB))
+    wide = torch.full((M, N + 3), -1.0, dtype=torch.float32, device=DEV)
+    mxq.mx_gemm_nt_mfma(dA, msA, dB, msB, out=wide[:, :N])
+    C = mxq.mx_gemm_nt_mfma(dA, msA, dB, msB)
+    torch.cuda.synchronize()
+    ref, absC = oracle.mx_gemm_nt(A, sA, B, sB, sa_strides=(K // 32, 1), sb_strides=(K // 32, 1),
+                                  threads=THREADS, with_abs=True)
+    _assert_close(wide[:, :N], ref, absC, K, torch.float32, "odd pitch")
+    _assert_close(C, ref, absC, K, torch.float32, "aligned")
+    assert torch.all(wide[:, N:] == -1.0)
+
+
+def test_ragged_tiles_of_the_large_tile_form():
+    """M and N that are odd multiples of 128 leave the 256 x 256 tiles ragged
+    at the bottom and the right (rows wrap onto valid rows for the loads,
+    their results are not stored); the contraction grouped over K uses the
+    same tiles."""
+    require_gpu()
+    say("mx_gemm_nt_mfma with ragged 256 x 256 tiles")
+    g = np.random.default_rng(14)
+    M, N, K = 384, 640, 384
+    A, B = _codes(g, (M, K)), _codes(g, (N, K))
+    sA = g.integers(118, 137, (M, K // 32), dtype=np.uint8)
+    sB = g.integers(118, 137, (N, K // 32), dtype=np.uint8)
+    out = torch.full((M, N + 8), 5.0, dtype=torch.bfloat16, device=DEV)
+    mxq.mx_gemm_nt_mfma(_dev(A), _dev(oracle.scales_to_mfma(sA)), _dev(B), _dev(oracle.scales_to_mfma(sB)),
+                        out=out[:, :N])
+    offs = np.array([128, 384], np.int32)
+    Cg = mxq.mx_grouped_gemm_k_mfma(_dev(A), _dev(oracle.scales_to_mfma(sA)), _dev(B),
+                                    _dev(oracle.scales_to_mfma(sB)), _dev(offs))
+    torch.cuda.synchronize()
+    ref, absC = oracle.mx_gemm_nt(A, sA, B, sB, sa_strides=(K // 32, 1), sb_strides=(K // 32, 1),
+                                  threads=THREADS, with_abs=True)
+    _assert_close(out[:, :N], ref, absC, K, torch.bfloat16, "ragged tiles")
+    assert torch.all(out[:, N:] == 5.0)
+    refg, absg = oracle.mx_grouped_gemm_k(A, sA, B, sB, offs, sa_strides=(K // 32, 1), sb_strides=(K // 32, 1),
+                                          threads=THREADS, with_abs=True)
+    for e in range(2):
+        _assert_close(Cg[e], refg[e], absg[e], 256 if e else 128, torch.float32, f"ragged group {e}")
 
 
 def test_rejections():

@@ -17,6 +17,14 @@
 // exact because the divisor is a power of two and |quotient| < 2^8, then
 // rounded half-to-even by v_rndne_f32; fp32 denormals are kept (no flush),
 // so subnormal inputs quantize exactly.
+//
+// Cache policy of the flat kernels (each byte is touched once): the pack
+// reads its input and writes q, max_exp and prime with the non-temporal
+// hint, the unpack writes its output with it.  Measured on MI355X, ordinary
+// write-back stores leave the memory-side cache full of dirty lines that the
+// next kernel pays for: in the sequence cast -> pack -> unpack the streaming
+// policy brings the step from 5.59 to 5.85 TB/s and the cast after it from
+// 206 to 196 us, and the unpack alone from 0.65-0.68 to 0.84 of peak.
 #include "mxq_kernels.h"
 #include "mx9_codec.h"
 
@@ -110,14 +118,19 @@ __device__ __forceinline__ void pack_piece(const void* __restrict__ xv, uint64_t
     using P = FlatPiece<kDtype>;
     const bool live = !kGuard || blk < nb;
     uint4 d = make_uint4(0u, 0u, 0u, 0u);
-    if (live) d = reinterpret_cast<const uint4*>(xv)[blk * P::kLanes + part];
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    if (live) {
+        const u4 v = __builtin_nontemporal_load(reinterpret_cast<const u4*>(xv) + blk * P::kLanes + part);
+        d = make_uint4(v.x, v.y, v.z, v.w);
+    }
     const P r = pack_flat_piece<kDtype>(d, part);
     if (live) {
         uint8_t* qb = reinterpret_cast<uint8_t*>(q) + blk * 16 + part * P::kElems;
-        if (P::kElems == 8) *reinterpret_cast<uint2*>(qb) = make_uint2(r.qd[0], r.qd[1]);
-        else *reinterpret_cast<uint32_t*>(qb) = r.qd[0];
-        if (part == 0) max_exp[blk] = uint8_t(r.S);
-        if (part == 1) prime[blk] = uint8_t(r.prime);
+        typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+        if (P::kElems == 8) __builtin_nontemporal_store(u2{r.qd[0], r.qd[1]}, reinterpret_cast<u2*>(qb));
+        else __builtin_nontemporal_store(r.qd[0], reinterpret_cast<uint32_t*>(qb));
+        if (part == 0) __builtin_nontemporal_store(uint8_t(r.S), max_exp + blk);
+        if (part == 1) __builtin_nontemporal_store(uint8_t(r.prime), prime + blk);
     }
 }
 
@@ -168,11 +181,11 @@ void mx9_unpack_flat(const int8_t* __restrict__ q, const uint8_t* __restrict__ m
             float4 o = make_float4(y[0], y[1], y[2], y[3]);
             if (S == 255u) o = make_float4(__uint_as_float(0x7FC00000u), __uint_as_float(0x7FC00000u),
                                            __uint_as_float(0x7FC00000u), __uint_as_float(0x7FC00000u));
-            reinterpret_cast<float4*>(yv)[blk * 4 + part] = o;
+            store_out16(reinterpret_cast<float4*>(yv) + blk * 4 + part, make_uint4(__float_as_uint(o.x), __float_as_uint(o.y), __float_as_uint(o.z), __float_as_uint(o.w)));
         } else {
             uint4 o = make_uint4(bf16_pair(y[0], y[1]), bf16_pair(y[2], y[3]), bf16_pair(y[4], y[5]), bf16_pair(y[6], y[7]));
             if (S == 255u) o = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-            reinterpret_cast<uint4*>(yv)[blk * 2 + part] = o;
+            store_out16(reinterpret_cast<uint4*>(yv) + blk * 2 + part, o);
         }
     }
 }

@@ -100,6 +100,14 @@ __device__ __forceinline__ void unpack16(uint4 qv, uint32_t S, uint32_t pr, floa
     }
 }
 
+// A 16-byte piece of unpacked output, written with the non-temporal hint:
+// the output is touched once, and ordinary write-back lines left in the
+// memory-side cache slow the kernel that runs next (measured on MI355X).
+__device__ __forceinline__ void store_out16(void* p, uint4 v) {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u4{v.x, v.y, v.z, v.w}, reinterpret_cast<u4*>(p));
+}
+
 __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
     const bf16x2 r = {__bf16(lo), __bf16(hi)};
     return __builtin_bit_cast(uint32_t, r);

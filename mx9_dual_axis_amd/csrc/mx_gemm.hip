@@ -395,8 +395,15 @@ void mx_gemm_pipe_kernel(GemmArgs p) {
     char* C = static_cast<char*>(p.C);
     bool zero = false;
     if (p.mode == 0) {
-        tm = blockIdx.x % p.tiles_m;
-        tn = blockIdx.x / p.tiles_m;
+        if (p.offs != nullptr) {
+            // row groups: consecutive workgroups take the column tiles of one
+            // row tile, so its activation rows are read from HBM once
+            tn = blockIdx.x % p.tiles_n;
+            tm = blockIdx.x / p.tiles_n;
+        } else {
+            tm = blockIdx.x % p.tiles_m;
+            tn = blockIdx.x / p.tiles_m;
+        }
         if (p.offs != nullptr) {                                // kTM == 128: one group unit
             const int64_t row = int64_t(tm) * P::kTM;
             int32_t g = 0;

@@ -309,7 +309,9 @@ __device__ __forceinline__ void mma_step(v4f (&acc)[MS][NS], const uint4* sa_lds
 // cores busy 30%.  This form changes four things:
 //   * wave tiles of 64 x (16 NS): NS = 8 (64 x 128, a 256 x 256 tile of 8
 //     waves, 2 per SIMD) reads a quarter fewer LDS bytes per instruction;
-//     row groups use NS = 4 (128 x 256 tiles, since a group unit is 128 rows);
+//     row groups use NS = 4 (128 x 256 tiles, since a group unit is 128 rows).
+//     128 x 128 wave tiles (4 waves, accumulators in the AGPRs) were slower:
+//     one wave per SIMD does not hide the LDS and barrier latency;
 //   * operands and the step's scale dwords go straight from global memory
 //     into LDS (buffer loads with the LDS destination); no registers stage
 //     them and no LDS writes are issued;
@@ -327,7 +329,6 @@ __device__ __forceinline__ void mma_step(v4f (&acc)[MS][NS], const uint4* sa_lds
 // which is what the waits count.
 // ---------------------------------------------------------------------------
 
-constexpr int kPipeThreads = 512;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -361,31 +362,36 @@ __device__ __forceinline__ void pipe_sync() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kLeft) : "memory");
 }
 
-// Configuration: WM x WN waves of 64 x 16 NS each; the tile is 64 WM x 16 NS WN.
-template <int WM, int NS>
+// Configuration: WM x WN waves of (16 MS) x (16 NS) each; the tile is
+// (16 MS WM) x (16 NS WN).  Every wave issues kLoads loads per step: its
+// share of the A and B pieces and kRpw scale runs (runs past the last repeat
+// it into spare slots).
+template <int MS, int NS, int WM, int WN>
 struct Pipe {
-    static constexpr int WN = 8 / WM;
-    static constexpr int kTM = 64 * WM, kTN = 16 * NS * WN;
+    static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
+    static constexpr int kTM = 16 * MS * WM, kTN = 16 * NS * WN;
+    static constexpr int kLA = 2 * MS / WN, kLB = 2 * NS / WM;   // 16-byte loads per wave and step
+    static constexpr int kRunsA = kTM / 64, kRuns = kTM / 64 + kTN / 64;
+    static constexpr int kRpw = (kRuns + kWaves - 1) / kWaves;    // scale runs per wave
     static constexpr uint32_t kA = 0, kB = uint32_t(kTM) * 128, kS = kB + uint32_t(kTN) * 128;
-    static constexpr uint32_t kStage = kS + 8 * 256;            // + 8 scale runs of 256 bytes
+    static constexpr uint32_t kStage = kS + uint32_t(kWaves * kRpw) * 256;
     static constexpr int kStages = (160 * 1024) / kStage >= 3 ? 3 : 2;
-    static constexpr int kLA = WM, kLB = NS * WN / 4;            // 16-byte loads per wave and step
-    static constexpr int kRunsA = WM, kRuns = WM + NS * WN / 4;  // scale runs (A groups, then B groups)
-    static constexpr int kLoads = kLA + kLB + 1;
+    static constexpr int kLoads = kLA + kLB + kRpw;
+    static_assert(kLA * WN == 2 * MS && kLB * WM == 2 * NS, "pieces divide evenly over the waves");
+    static_assert(kStages == 2 || kLoads < 16, "vmcnt immediate");
 };
 
-template <int kOut, int WM, int NS>
-__global__ __launch_bounds__(kPipeThreads)
+template <int kOut, int MS, int NS, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, WM * WN >= 8 ? 2 : 1)
 void mx_gemm_pipe_kernel(GemmArgs p) {
-    using P = Pipe<WM, NS>;
+    using P = Pipe<MS, NS, WM, WN>;
     constexpr int kEsz = kOut == 0 ? 4 : 2;
     constexpr int kPitch = 16 * NS * kEsz + 16;                 // staged result row, bytes
-    static_assert(P::kRuns <= 8, "one scale run per wave");
     __shared__ __attribute__((aligned(16))) uint8_t lds[P::kStages * P::kStage];
 
     const uint32_t t = threadIdx.x, lane = t & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const uint32_t wm = wave / P::WN, wn = wave % P::WN;
+    const uint32_t wm = wave / WN, wn = wave % WN;
 
     // ---- which tile, which group, which range of the contraction ----
     uint32_t tm, tn;
@@ -436,15 +442,20 @@ void mx_gemm_pipe_kernel(GemmArgs p) {
     const uint32_t b_mask = uint32_t(min(int64_t(P::kTN), p.N - n0)) - 1u;
     const v4i ra = pipe_rsrc(p.A + m0 * p.lda);
     const v4i rb = pipe_rsrc(B + n0 * p.ldb);
-    // scale run of this wave (A groups first, then B groups; groups past a
-    // ragged last tile clamp to the last one; waves past the runs repeat the last)
-    const uint32_t run = wave < uint32_t(P::kRuns) ? wave : uint32_t(P::kRuns - 1);
+    // scale runs of this wave (A groups first, then B groups; groups past a
+    // ragged last tile clamp to the last one; runs past the last repeat it)
     const int64_t ga_max = p.M / 64 - 1 - m0 / 64, gb_max = p.N / 64 - 1 - n0 / 64;
     const v4i rs_a = pipe_rsrc(p.sA + (m0 / 64) * p.sa_rs);
     const v4i rs_b = pipe_rsrc(sB + (n0 / 64) * p.sb_rs);
-    const bool run_a = run < uint32_t(P::kRunsA);
-    const uint32_t s_run_off = run_a ? uint32_t(min(int64_t(run), ga_max)) * uint32_t(p.sa_rs)
-                                     : uint32_t(min(int64_t(run - P::kRunsA), gb_max)) * uint32_t(p.sb_rs);
+    bool run_a[P::kRpw];
+    uint32_t s_run_off[P::kRpw];
+#pragma unroll
+    for (int r = 0; r < P::kRpw; ++r) {
+        const uint32_t run = min(wave * uint32_t(P::kRpw) + uint32_t(r), uint32_t(P::kRuns - 1));
+        run_a[r] = run < uint32_t(P::kRunsA);
+        s_run_off[r] = run_a[r] ? uint32_t(min(int64_t(run), ga_max)) * uint32_t(p.sa_rs)
+                                : uint32_t(min(int64_t(run - P::kRunsA), gb_max)) * uint32_t(p.sb_rs);
+    }
     const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(lds));
 #define MXQ_PIPE_ISSUE(step)                                                                     \
     do {                                                                                         \
@@ -458,13 +469,14 @@ void mx_gemm_pipe_kernel(GemmArgs p) {
             const uint32_t j_ = uint32_t(P::kLB) * wave + q_;                                    \
             pipe_load16(rb, st_ + P::kB + 1024u * j_, vob, ((8u * j_) & b_mask) * ldb + k_);     \
         }                                                                                        \
-        pipe_load4(run_a ? rs_a : rs_b, st_ + P::kS + 256u * wave, 4u * lane,                    \
-                   s_run_off + (k_ / uint32_t(kTile)) * 256u);                                   \
+        _Pragma("unroll") for (int r_ = 0; r_ < P::kRpw; ++r_)                                   \
+            pipe_load4(run_a[r_] ? rs_a : rs_b, st_ + P::kS + 256u * (wave * P::kRpw + r_), 4u * lane, \
+                       s_run_off[r_] + (k_ / uint32_t(kTile)) * 256u);                           \
     } while (0)
 
-    v4f acc[4][NS];
+    v4f acc[MS][NS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MS; ++i)
 #pragma unroll
         for (int j = 0; j < NS; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
@@ -474,27 +486,33 @@ void mx_gemm_pipe_kernel(GemmArgs p) {
     for (int64_t s = 0; s < n; ++s) {
         // step s's loads are in LDS (the later issued steps may still be in
         // flight) and the stage step s - 1 used is free
-        if (P::kStages == 3 && s + 1 < n) pipe_sync<P::kLoads>();
-        else pipe_sync<0>();
+        if constexpr (P::kStages == 3) {
+            if (s + 1 < n) pipe_sync<P::kLoads>();
+            else pipe_sync<0>();
+        } else {
+            pipe_sync<0>();
+        }
         if (s + P::kStages - 1 < n) MXQ_PIPE_ISSUE(s + P::kStages - 1);
         const uint8_t* st = lds + uint32_t(s % P::kStages) * P::kStage;
-        int sa[1], sb[NS / 4];
-        sa[0] = *reinterpret_cast<const int*>(st + P::kS + 256u * wm + 4u * lane);
+        int sa[MS / 4], sb[NS / 4];
+#pragma unroll
+        for (int j = 0; j < MS / 4; ++j)
+            sa[j] = *reinterpret_cast<const int*>(st + P::kS + 256u * ((MS / 4) * wm + j) + 4u * lane);
 #pragma unroll
         for (int j = 0; j < NS / 4; ++j)
             sb[j] = *reinterpret_cast<const int*>(st + P::kS + 256u * (P::kRunsA + (NS / 4) * wn + j) + 4u * lane);
-        mma_step<4, NS>(acc, reinterpret_cast<const uint4*>(st + P::kA), reinterpret_cast<const uint4*>(st + P::kB),
-                        wm * 64u, wn * 16u * NS, lane, sa, sb, std::make_integer_sequence<int, NS>{});
+        mma_step<MS, NS>(acc, reinterpret_cast<const uint4*>(st + P::kA), reinterpret_cast<const uint4*>(st + P::kB),
+                         wm * 16u * MS, wn * 16u * NS, lane, sa, sb, std::make_integer_sequence<int, NS>{});
     }
 #undef MXQ_PIPE_ISSUE
     __syncthreads();
 
     // ---- epilogue through LDS: 16 rows of the wave tile at a time, 16-byte non-temporal stores ----
-    // acc[i][j][v] is C[m0 + 64 wm + 16 i + 4 (lane / 16) + v][n0 + 16 NS wn + 16 j + lane % 16]
+    // acc[i][j][v] is C[m0 + 16 MS wm + 16 i + 4 (lane / 16) + v][n0 + 16 NS wn + 16 j + lane % 16]
     uint8_t* ep = lds + wave * (16 * kPitch);
     constexpr int kPieces = 16 * NS * kEsz / 16;               // 16-byte pieces per staged row
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MS; ++i) {
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
 #pragma unroll
@@ -508,7 +526,7 @@ void mx_gemm_pipe_kernel(GemmArgs p) {
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);                     // lgkmcnt(0): this wave's staging writes done
         __builtin_amdgcn_wave_barrier();
-        const int64_t row0 = m0 + 64 * wm + 16 * i;
+        const int64_t row0 = m0 + 16 * MS * wm + 16 * i;
         const int64_t col0 = n0 + 16 * NS * wn;
 #pragma unroll
         for (int q = 0; q < 16 * kPieces / 64; ++q) {
@@ -551,19 +569,19 @@ hipError_t launch_mx_gemm(const uint8_t* A, int64_t lda, const uint8_t* sA, int6
         // row groups: 128-row tiles (one group unit); otherwise 256 x 256
         const bool row_groups = mode == 0 && offs != nullptr;
         if (row_groups) {
-            using P = Pipe<2, 4>;
+            using P = Pipe<4, 4, 2, 4>;
             p.tiles_m = uint32_t(M / P::kTM);
             p.tiles_n = uint32_t((N + P::kTN - 1) / P::kTN);
-            const dim3 grid(p.tiles_m * p.tiles_n), block(kPipeThreads);
-            if (out_dtype == 0) hipLaunchKernelGGL((mx_gemm_pipe_kernel<0, 2, 4>), grid, block, 0, stream, p);
-            else hipLaunchKernelGGL((mx_gemm_pipe_kernel<1, 2, 4>), grid, block, 0, stream, p);
+            const dim3 grid(p.tiles_m * p.tiles_n), block(P::kThreads);
+            if (out_dtype == 0) hipLaunchKernelGGL((mx_gemm_pipe_kernel<0, 4, 4, 2, 4>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((mx_gemm_pipe_kernel<1, 4, 4, 2, 4>), grid, block, 0, stream, p);
         } else {
-            using P = Pipe<4, 8>;
+            using P = Pipe<4, 8, 4, 2>;
             p.tiles_m = uint32_t((M + P::kTM - 1) / P::kTM);
             p.tiles_n = uint32_t((N + P::kTN - 1) / P::kTN);
-            const dim3 grid(p.tiles_m * p.tiles_n * uint32_t(mode == 1 ? G : 1)), block(kPipeThreads);
-            if (out_dtype == 0) hipLaunchKernelGGL((mx_gemm_pipe_kernel<0, 4, 8>), grid, block, 0, stream, p);
-            else hipLaunchKernelGGL((mx_gemm_pipe_kernel<1, 4, 8>), grid, block, 0, stream, p);
+            const dim3 grid(p.tiles_m * p.tiles_n * uint32_t(mode == 1 ? G : 1)), block(P::kThreads);
+            if (out_dtype == 0) hipLaunchKernelGGL((mx_gemm_pipe_kernel<0, 4, 8, 4, 2>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((mx_gemm_pipe_kernel<1, 4, 8, 4, 2>), grid, block, 0, stream, p);
         }
         return hipGetLastError();
     }

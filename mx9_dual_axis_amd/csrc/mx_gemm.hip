@@ -17,9 +17,13 @@
 // [L % 16] is element v of lane L's four accumulators.  The same layout for
 // A and B means each lane reads two 16-byte pieces of one stored row.
 //
-// Work decomposition: one workgroup (4 wave64s) per 128 x 128 tile of C;
-// wave w computes the 64 x 64 quarter (w / 2, w % 2) as 4 x 4 instructions
-// per 128-wide step of the contraction.
+// Two kernels.  mx_gemm_kernel (below) takes strided scale views, i.e. the
+// cast's plain scale layouts; mx_gemm_pipe_kernel (further below) takes the
+// matrix-core scale layout and is the fast path.
+//
+// mx_gemm_kernel: one workgroup (4 wave64s) per 128 x 128 tile of C; wave w
+// computes the 64 x 64 quarter (w / 2, w % 2) as 4 x 4 instructions per
+// 128-wide step of the contraction.
 //   * staging: the A and B tiles of a step (128 rows x 128 bytes each) are
 //     loaded with 16-byte global loads (a wave covers eight whole 128-byte
 //     rows) into double-buffered LDS; the 16-byte chunk index of a row is
@@ -48,7 +52,6 @@ namespace {
 
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
-
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -303,7 +306,7 @@ __device__ __forceinline__ void mma_step(v4f (&acc)[MS][NS], const uint4* sa_lds
 // ---------------------------------------------------------------------------
 // Form for scales in the matrix-core layout (the default consumer path).
 //
-// Measured on MI355X, the first kernel is bound by LDS throughput: a 64 x 64
+// Measured on MI355X, mx_gemm_kernel is bound by LDS throughput: a 64 x 64
 // wave tile reads 16 KB of fragments per 16 instructions.  Counters showed
 // the LDS data FIFO full 58% of cycles, no bank conflicts and the matrix
 // cores busy 30%.  This form changes four things:
@@ -325,10 +328,9 @@ __device__ __forceinline__ void mma_step(v4f (&acc)[MS][NS], const uint4* sa_lds
 //     rows with non-temporal stores (the weight gradient, whose groups are
 //     short, is bound by writing C).
 // Each wave issues the same number of loads per step (its A and B pieces
-// and one scale run; waves past the runs repeat the last into a spare slot),
-// which is what the waits count.
+// and its scale runs; runs past the last repeat it into a spare slot), which
+// is what the waits count.
 // ---------------------------------------------------------------------------
-
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -354,8 +356,8 @@ __device__ __forceinline__ void pipe_load4(v4i r, uint32_t lds, uint32_t voff, u
                  : "memory");
 }
 
-// Wait until at most kOut loads are outstanding and this wave's LDS reads
-// are done, then synchronize the workgroup.
+// Wait until at most kLeft of this wave's loads are outstanding and its LDS
+// reads are done, then synchronize the workgroup.
 template <int kLeft>
 __device__ __forceinline__ void pipe_sync() {
     static_assert(kLeft >= 0 && kLeft < 16, "vmcnt immediate");

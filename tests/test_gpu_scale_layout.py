@@ -252,3 +252,96 @@ def test_rejections():
     assert ei.value.status == 7
     with pytest.raises(ValueError):
         mxq.mx_quantize_2d_dual(torch.zeros((128, 128), dtype=torch.bfloat16, device=dev), scale_layout="swizzled")
+
+
+# ---------------------------------------------------------------- full sizes
+
+def test_full_size_grouped_cast_and_contractions_in_the_matrix_core_layout():
+    """The workloads the bench times in the matrix-core layout: the grouped
+    cast of bf16 [16384, 5120] (64 groups), its outputs consumed by the
+    row-grouped forward (64 experts of [2048, 5120]) and the contraction-
+    grouped weight gradient (dY [2048, 16384] over the token groups).  The
+    cast's scale bytes of sampled rows and slabs equal the oracle's, placed
+    by the layout's index function; sampled output rows of every few groups
+    meet the oracle's contraction within the bound."""
+    dev = require_gpu()
+    say("full size: grouped cast [16384, 5120] (mfma layout) -> grouped contractions, sampled")
+    xb, offs = synth.grouped()
+    M, K = xb.shape
+    N, E = 2048, len(offs)
+    od = _dev(offs)
+    q_row, s_row, q_col, s_col = mxq.mx_quantize_grouped(bf16_to_dev(xb), od, scale_layout="mfma")
+    torch.cuda.synchronize()
+    hs_row, hs_col = host(s_row), host(s_col)
+    # scales of sampled rows (rowwise) and slabs (colwise) against the oracle
+    rows = np.array([0, 1, 4095, 8191, 12287, 12288, M - 1])
+    _, sr = oracle.mxfp8_rowwise(np.ascontiguousarray(xb[rows]), threads=THREADS)
+    r, b = np.meshgrid(rows, np.arange(K // 32), indexing="ij")
+    assert np.array_equal(hs_row[oracle.mfma_scale_index(r, b, K // 32)], sr)
+    tail = int(offs[-1]) // 32
+    for i in (0, 200, tail - 1, tail, M // 32 - 1):
+        _, sc = oracle.mxfp8_colwise(np.ascontiguousarray(xb[32 * i:32 * i + 32]), threads=THREADS)
+        want = sc[0] if i < tail else np.zeros_like(sc[0])
+        n = np.arange(K)
+        assert np.array_equal(hs_col[oracle.mfma_scale_index(n, np.full_like(n, i), M // 32)], want), f"slab {i}"
+    hq_row, hq_col = host(q_row), host(q_col)
+    sr_plain = oracle.scales_from_mfma(hs_row, M, K // 32)          # [M, K/32]
+    sc_plain = oracle.scales_from_mfma(hs_col, K, M // 32)          # [K, M/32]
+
+    g = np.random.default_rng(15)
+    W = np.stack([_codes(g, (N, K)) for _ in range(E)])
+    sW = g.integers(118, 137, (E, N, K // 32), dtype=np.uint8)
+    sWm = np.stack([oracle.scales_to_mfma(sW[e]) for e in range(E)])
+    Y = host(mxq.mx_grouped_gemm_rows_mfma(q_row, s_row, _dev(W), _dev(sWm), od))
+    lo = 0
+    for e, hi in enumerate(offs):
+        if hi > lo and e % 7 == 0:
+            for rr in (int(lo), int(hi) - 1):
+                ref, absC = oracle.mx_gemm_nt(hq_row[rr:rr + 1], sr_plain[rr:rr + 1], W[e], sW[e],
+                                              sa_strides=(K // 32, 1), sb_strides=(K // 32, 1), threads=THREADS,
+                                              with_abs=True)
+                _assert_close(torch.from_numpy(Y[rr:rr + 1]), ref, absC, K, torch.float32, f"forward row {rr}")
+        lo = hi
+    assert np.all(Y[int(offs[-1]):] == 0)
+    del Y, W
+
+    dY = _codes(g, (N, M))
+    sdY = g.integers(118, 137, (N, M // 32), dtype=np.uint8)
+    dW = mxq.mx_grouped_gemm_k_mfma(q_col, s_col, _dev(dY), _dev(oracle.scales_to_mfma(sdY)), od,
+                                    out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    krows = [0, 2047, K - 1]
+    lo = 0
+    for e, hi in enumerate(offs):
+        if e % 9 == 0 or e == E - 1:
+            got = dW[e, krows]
+            ref = np.zeros((len(krows), N))
+            absC = np.zeros((len(krows), N))
+            if hi > lo:
+                for j, kr in enumerate(krows):
+                    r1, a1 = oracle.mx_gemm_nt(hq_col[kr:kr + 1], sc_plain[kr:kr + 1], dY, sdY,
+                                               sa_strides=(M // 32, 1), sb_strides=(M // 32, 1),
+                                               k0=int(lo), k1=int(hi), with_abs=True)
+                    ref[j], absC[j] = r1[0], a1[0]
+            _assert_close(got, ref, absC, max(int(hi - lo), 1), torch.bfloat16, f"weight gradient group {e}")
+        lo = hi
+
+
+def test_full_size_dense_contraction_sampled():
+    """The dense [8192]^3 product the bench times, in the matrix-core layout:
+    sampled rows (first, last, and rows of different 256-row tiles and wave
+    quarters) against the oracle."""
+    require_gpu()
+    say("full size: dense [8192]^3 contraction (mfma layout), sampled rows")
+    D = 8192
+    g = np.random.default_rng(16)
+    A, B = _codes(g, (D, D)), _codes(g, (D, D))
+    sA = g.integers(118, 137, (D, D // 32), dtype=np.uint8)
+    sB = g.integers(118, 137, (D, D // 32), dtype=np.uint8)
+    C = mxq.mx_gemm_nt_mfma(_dev(A), _dev(oracle.scales_to_mfma(sA)), _dev(B), _dev(oracle.scales_to_mfma(sB)),
+                            out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for rr in (0, 77, 4096 + 200, D - 1):
+        ref, absC = oracle.mx_gemm_nt(A[rr:rr + 1], sA[rr:rr + 1], B, sB, sa_strides=(D // 32, 1),
+                                      sb_strides=(D // 32, 1), threads=THREADS, with_abs=True)
+        _assert_close(C[rr:rr + 1], ref, absC, D, torch.bfloat16, f"dense row {rr}")

@@ -10,12 +10,10 @@ Prints ONE JSON line.  ``value`` is the step's algorithmic bytes (what the
 method must read and write, per kernel) divided by the step time, in GB/s.
 ``roofline`` describes the dominant operation, the dual-axis cast: its
 algorithmic bytes per call over its average call time from HIP events on the
-launch stream (the call is the main kernel plus, for N <= 16256 with
-N % 512 == 0, the small kernel that transposes the staged rowwise scales),
-against MI355X's 8 TB/s HBM peak.  ``traffic`` is the HBM byte count per
-call (both kernels) from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-summary, reported only while the kernel source matches the source those
-counters were taken on.  ``cpu_baseline`` times the CPU oracle on a bounded
+launch stream (the call is one kernel), against MI355X's 8 TB/s HBM peak.
+``traffic`` is the HBM byte count per call from the committed rocprofv3
+FETCH_SIZE / WRITE_SIZE summary, reported only while the kernel source
+matches the source those counters were taken on.  ``cpu_baseline`` times the CPU oracle on a bounded
 sample of the same workload (a multithreaded leg of about ten seconds and a
 single-thread leg).
 
@@ -25,10 +23,10 @@ last-level cache cannot serve a call from the previous one: the dense cast of
 the mixed-magnitude bf16 [8192, 7168] matrix, the grouped cast of bf16
 [16384, 5120] with 64 groups, and MX9 pack/unpack of the fp32 and bf16
 [4096, 14336] weights in three forms: three tensors along the last axis,
-one tensor of 18-byte records, and three tensors along axis 0.  It also holds the dual-axis cast of the stress matrix
-timed alone (back-to-back calls): inside the step the cast starts while the
-previous step's MX9 unpack writes are still draining to HBM, so its in-step
-time is longer than its time alone.
+one tensor of 18-byte records, and three tensors along axis 0; the casts and
+contractions in the matrix-core scale layout; and the dual-axis cast of the
+stress matrix timed alone (back-to-back calls), to compare with its time
+inside the step.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--skip-cpu] [--skip-configs]
 """
@@ -509,7 +507,7 @@ def main():
                    "step_algorithmic_bytes": int(step_bytes)},
         "roofline": {"bound": "hbm", "achieved": dual["GB_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(dual["GB_s"] / PEAK_HBM_GBS, 4), "traffic": committed_traffic(),
-                     "kernel": "dual_axis_kernel<false, 1> + srow_permute_kernel (one dual-axis call)",
+                     "kernel": "dual_axis_kernel<false, 0> (one dual-axis call)",
                      "algorithmic_bytes_per_launch": dual["bytes"],
                      "avg_launch_us": dual["us"]},
         "kernels": kernels,

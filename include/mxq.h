@@ -77,8 +77,7 @@ enum { MX_OFFS_OK = 0, MX_OFFS_ORDER = 1, MX_OFFS_ALIGN = 2, MX_OFFS_BOUNDS = 3 
  * MX_E_SHAPE (M or N negative, not a multiple of 128, or above 2^24),
  * MX_E_STRIDE (ld_x < N, not a multiple of 8, or above 2^24), MX_E_ALIGN
  * (any pointer not 16-byte aligned), MX_E_OVERLAP.  M == 0 or N == 0 is a
- * no-op.  The call may enqueue two kernels on the stream; s_row is complete
- * once both have run.
+ * no-op.  The call enqueues one kernel on the stream.
  */
 int mx_quantize_2d_dual(const uint16_t *x, int64_t M, int64_t N, int64_t ld_x,
                         int32_t block_size, int32_t scaling_mode,

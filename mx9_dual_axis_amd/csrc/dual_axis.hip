@@ -36,12 +36,15 @@
 //              the input and of both outputs over the HBM channels; a smaller
 //              call goes down whole tile columns (column-major), which the
 //              cache serves better (measured on the workloads' shapes).
-//   * s_row  : a tile owns only 4 scale bytes per row, and 128 scattered 4-byte
-//              stores per tile cost more than the rest of the tile's writes.
-//              When N <= 16256 and N % 512 == 0, each tile instead writes its
-//              512 scale bytes as one contiguous run inside its band's s_row
-//              rows (a band's rows are one contiguous range), and a second,
-//              small kernel transposes each band in place through LDS.
+//   * s_row  : a tile owns 4 scale bytes of each of its 128 rows, written as
+//              one 4-byte store per row.  Consecutive workgroups go to
+//              consecutive XCDs, so with a tile-row count that is a multiple
+//              of 8 (every workload here) the order below keeps all tiles of
+//              a tile row on one XCD and close in time, and that L2 merges
+//              the stores into whole sectors: WRITE_SIZE of a stress call is
+//              within 1.4% of the algorithmic bytes (an earlier order showed
+//              each store as a 32-byte write, and a staged layout with a
+//              second, transposing kernel was slower than this).
 //   * caching: the input and the outputs are touched once, and how their
 //              lines travel through the L2 and the 256 MB memory-side cache
 //              decides the speed far more than the arithmetic does.  The tile
@@ -79,13 +82,11 @@ namespace {
 
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
-constexpr int64_t kMaxStagedN = 16256;   // 127 tiles x 129 dwords = 65,532 bytes of LDS
 constexpr double kMemorySideCacheBytes = 256.0 * 1024 * 1024;   // MI355X last-level (MALL) capacity
 
-// How a call writes s_row (s_col is plain unless the matrix-core layout is asked for).
-constexpr int kScalesDirect = 0;   // [M][N/32], 4-byte stores per tile row
-constexpr int kScalesStaged = 1;   // [M][N/32], contiguous per-tile runs put in order by srow_permute_kernel
-constexpr int kScalesMfma = 2;     // both tensors in the matrix-core layout
+// How a call writes its scales.
+constexpr int kScalesPlain = 0;    // s_row [M][N/32], s_col [M/32][N]
+constexpr int kScalesMfma = 1;     // both tensors in the matrix-core layout
 
 typedef short v2i16 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -255,13 +256,6 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
             const int64_t run = (2 * int64_t(tm) + (t >> 4)) * tiles_n + tn;
             *reinterpret_cast<uint4*>(s_row + run * 256 + 16 * (t & 15u)) = reinterpret_cast<const uint4*>(lds_srow)[t];
         }
-    } else if (kScales == kScalesStaged) {
-        // Sector-complete staging: the 8 tiles of a group share the 128 x 32-byte
-        // s_row region of their rows; tile jt writes its 512 bytes as pieces
-        // 16*jt .. 16*jt+15 (piece P = the region's row P, 8 of this tile's rows
-        // per piece).  A second pass puts every piece into final row order.
-        if (t < 32)
-            *reinterpret_cast<uint4*>(s_row + m0 * (N / 32) + int64_t(tn) * 512 + 16 * t) = reinterpret_cast<const uint4*>(lds_srow)[t];
     } else if (t < kTile) {
         *reinterpret_cast<uint32_t*>(s_row + (m0 + t) * (N / 32) + n0 / 32) = lds_srow[t];
     }
@@ -333,39 +327,6 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
     }
 }
 
-// Second pass of the staged s_row layout.  The main kernel writes each
-// tile's 128 rows x 4 scale bytes as one contiguous 512-byte run at offset
-// 512 * tn inside its band's s_row rows (a band's 128 rows of s_row are one
-// contiguous 4N-byte range), i.e. the band holds a [tiles_n][128] array of
-// dwords.  Here one workgroup per band reads the whole range into LDS and
-// writes it back transposed to the final [128][tiles_n] row layout.
-constexpr int kPermThreads = 1024;
-
-__global__ __launch_bounds__(kPermThreads)
-void srow_permute_kernel(uint8_t* __restrict__ s_row, int64_t N) {
-    extern __shared__ uint32_t lds_band[];               // [tiles_n][129] dwords
-    const uint32_t tiles_n = uint32_t(N / kTile);
-    const uint32_t nq = tiles_n * 32;                     // 16-byte chunks in the band
-    uint8_t* band = s_row + int64_t(blockIdx.x) * kTile * (N / 32);
-    for (uint32_t i = threadIdx.x; i < nq; i += kPermThreads) {
-        const uint4 v = reinterpret_cast<const uint4*>(band)[i];
-        const uint32_t tn = i >> 5, r = (i & 31u) * 4u;   // 32 chunks per tile
-        uint32_t* d = lds_band + tn * 129u + r;
-        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-    }
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < nq; i += kPermThreads) {
-        const uint32_t f = i * 4u;                        // first final dword of this chunk
-        const uint32_t r = f / tiles_n, tn = f - r * tiles_n;
-        uint4 v;
-        v.x = lds_band[(tn + 0) * 129u + r];
-        v.y = lds_band[(tn + 1) * 129u + r];
-        v.z = lds_band[(tn + 2) * 129u + r];
-        v.w = lds_band[(tn + 3) * 129u + r];
-        reinterpret_cast<uint4*>(band)[i] = v;
-    }
-}
-
 __global__ __launch_bounds__(kThreads)
 void offs_validate_kernel(const int32_t* __restrict__ offs, int32_t G, int64_t M, int32_t* __restrict__ err) {
     validate_offsets(offs, G, M, err);
@@ -379,10 +340,7 @@ hipError_t launch_dual_axis(const uint16_t* x, int64_t M, int64_t N, int64_t ld_
                             bool mfma_scales, hipStream_t stream) {
     const uint32_t tiles_n = uint32_t(N / kTile);
     const uint32_t tiles = uint32_t((M / kTile) * (N / kTile));
-    // the staged s_row layout needs the band to fit the permute pass's LDS
-    // and its chunks to hold 4 whole tiles
-    const int scales = mfma_scales ? kScalesMfma
-                       : (N <= kMaxStagedN && N % 512 == 0) ? kScalesStaged : kScalesDirect;
+    const int scales = mfma_scales ? kScalesMfma : kScalesPlain;
     // q_row streaming share by the call's size against the memory-side cache
     const double call_bytes = 4.0625 * double(M) * double(N);
     const bool large = call_bytes > 2.0 * kMemorySideCacheBytes;
@@ -398,18 +356,12 @@ hipError_t launch_dual_axis(const uint16_t* x, int64_t M, int64_t N, int64_t ld_
                        s_col, tiles_n, tiles, row_stream, large, offs, G, err)
     if (grouped) {
         if (scales == kScalesMfma) MXQ_LAUNCH(true, kScalesMfma);
-        else if (scales == kScalesStaged) MXQ_LAUNCH(true, kScalesStaged);
-        else MXQ_LAUNCH(true, kScalesDirect);
+        else MXQ_LAUNCH(true, kScalesPlain);
     } else {
         if (scales == kScalesMfma) MXQ_LAUNCH(false, kScalesMfma);
-        else if (scales == kScalesStaged) MXQ_LAUNCH(false, kScalesStaged);
-        else MXQ_LAUNCH(false, kScalesDirect);
+        else MXQ_LAUNCH(false, kScalesPlain);
     }
 #undef MXQ_LAUNCH
-    if (scales == kScalesStaged) {
-        const uint32_t lds = uint32_t(N / kTile) * 129u * 4u;
-        hipLaunchKernelGGL(srow_permute_kernel, dim3(uint32_t(M / kTile)), dim3(kPermThreads), lds, stream, s_row, N);
-    }
     return hipGetLastError();
 }
 

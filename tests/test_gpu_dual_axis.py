@@ -50,14 +50,16 @@ def test_dense_parity(M, N, kind, seed):
 
 
 @pytest.mark.parametrize("M,N", [
-    (128, 15872),    # the widest shape whose rowwise scales go through the band transpose
-    (256, 16384),    # wider: rowwise scales written directly
-    (384, 2560),     # N % 512 == 0, staged
-    (128, 1152),     # N % 512 != 0, direct
+    (128, 15872),    # one tile row, 124 tiles across (tile-row count not a multiple of 8)
+    (256, 16384),    # wide rows
+    (384, 2560),     # three tile rows
+    (1152, 1152),    # 9 x 9 tiles: consecutive tiles of a tile row on different XCDs
 ])
-def test_rowwise_scale_paths(M, N):
+def test_rowwise_scale_shapes(M, N):
+    """s_row is written with one 4-byte store per tile row; shapes whose tile
+    rows do and do not stay on one XCD give the same bytes."""
     dev = require_gpu()
-    say(f"s_row paths M={M} N={N}")
+    say(f"s_row shapes M={M} N={N}")
     xb = synth.mixed_rows(M, N, M + N)
     out = _dirty_outputs(M, N, dev)
     mxq.mx_quantize_2d_dual(bf16_to_dev(xb), out=out)

@@ -114,7 +114,7 @@ def test_repeatable_and_dirty_buffers():
         assert torch.equal(u, v)
 
 
-@pytest.mark.parametrize("N", [384, 1024])   # 1024: rowwise scales staged (two kernels per call)
+@pytest.mark.parametrize("N", [384, 1024])
 def test_runs_on_the_callers_stream_and_in_a_graph(N):
     dev = require_gpu()
     say(f"stream and graph capture N={N}")
@@ -141,7 +141,7 @@ def test_runs_on_the_callers_stream_and_in_a_graph(N):
         _assert_equal(out, want, f"graph replay {rep}")
 
 
-@pytest.mark.parametrize("N", [256, 1024])   # 1024: rowwise scales staged
+@pytest.mark.parametrize("N", [256, 1024])
 def test_grouped_parity_and_tail(N):
     dev = require_gpu()
     M = 1024

@@ -345,3 +345,62 @@ def test_full_size_dense_contraction_sampled():
         ref, absC = oracle.mx_gemm_nt(A[rr:rr + 1], sA[rr:rr + 1], B, sB, sa_strides=(D // 32, 1),
                                       sb_strides=(D // 32, 1), threads=THREADS, with_abs=True)
         _assert_close(C[rr:rr + 1], ref, absC, D, torch.bfloat16, f"dense row {rr}")
+
+
+def test_pipeline_edge_cases():
+    """The pipelined contraction at its boundaries: one 128-wide step
+    (nothing prefetched), one-step groups, groups that are all empty (every
+    output zero), a forward whose rows are all past the last offset, and
+    three-stage row groups with exactly two steps."""
+    require_gpu()
+    say("pipelined contraction edge cases")
+    g = np.random.default_rng(17)
+
+    def mats(M, N, K):
+        A, B = _codes(g, (M, K)), _codes(g, (N, K))
+        sA = g.integers(118, 137, (M, K // 32), dtype=np.uint8)
+        sB = g.integers(118, 137, (N, K // 32), dtype=np.uint8)
+        return A, B, sA, sB
+
+    # one step, fp32 and bf16
+    A, B, sA, sB = mats(256, 384, 128)
+    for od in (torch.float32, torch.bfloat16):
+        C = mxq.mx_gemm_nt_mfma(_dev(A), _dev(oracle.scales_to_mfma(sA)), _dev(B), _dev(oracle.scales_to_mfma(sB)),
+                                out_dtype=od)
+        torch.cuda.synchronize()
+        ref, absC = oracle.mx_gemm_nt(A, sA, B, sB, sa_strides=(4, 1), sb_strides=(4, 1), threads=THREADS,
+                                      with_abs=True)
+        _assert_close(C, ref, absC, 128, od, f"K = 128 {od}")
+
+    # contraction groups of one step each, and all-empty groups
+    A, B, sA, sB = mats(256, 256, 512)
+    mA, mB = _dev(oracle.scales_to_mfma(sA)), _dev(oracle.scales_to_mfma(sB))
+    offs = np.array([128, 256, 384, 512], np.int32)
+    C = mxq.mx_grouped_gemm_k_mfma(_dev(A), mA, _dev(B), mB, _dev(offs))
+    torch.cuda.synchronize()
+    ref, absC = oracle.mx_grouped_gemm_k(A, sA, B, sB, offs, sa_strides=(16, 1), sb_strides=(16, 1),
+                                         threads=THREADS, with_abs=True)
+    for e in range(4):
+        _assert_close(C[e], ref[e], absC[e], 128, torch.float32, f"one-step group {e}")
+    Z = mxq.mx_grouped_gemm_k_mfma(_dev(A), mA, _dev(B), mB, _dev(np.zeros(3, np.int32)))
+    torch.cuda.synchronize()
+    assert torch.all(Z == 0)
+
+    # row groups: every row past the last offset, then two-step rows
+    E = 3
+    Bw = np.stack([_codes(g, (256, 256)) for _ in range(E)])
+    sBw = g.integers(118, 137, (E, 256, 8), dtype=np.uint8)
+    sBm = _dev(np.stack([oracle.scales_to_mfma(sBw[e]) for e in range(E)]))
+    A2 = _codes(g, (384, 256))
+    sA2 = g.integers(118, 137, (384, 8), dtype=np.uint8)
+    out = torch.full((384, 256), 3.0, dtype=torch.float32, device=DEV)
+    mxq.mx_grouped_gemm_rows_mfma(_dev(A2), _dev(oracle.scales_to_mfma(sA2)), _dev(Bw), sBm,
+                                  _dev(np.zeros(E, np.int32)), out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+    offs2 = np.array([128, 128, 384], np.int32)
+    Y = mxq.mx_grouped_gemm_rows_mfma(_dev(A2), _dev(oracle.scales_to_mfma(sA2)), _dev(Bw), sBm, _dev(offs2))
+    torch.cuda.synchronize()
+    ref, absC = oracle.mx_grouped_gemm_rows(A2, sA2, Bw, sBw, offs2, sa_strides=(8, 1), sb_strides=(8, 1),
+                                            threads=THREADS, with_abs=True)
+    _assert_close(Y, ref, absC, 256, torch.float32, "two-step row groups")

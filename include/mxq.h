@@ -351,6 +351,26 @@ int mx_grouped_gemm_k_mfma(const uint8_t *A, int64_t lda, const uint8_t *sA, con
                            const uint8_t *sB, const int32_t *offs, int32_t G, int64_t M, int64_t N, int64_t K,
                            void *C, int64_t ldc, int64_t c_gs, int32_t out_dtype, void *stream);
 
+/*
+ * mx_scales_to_mfma -- rewrite rows x blocks E8M0 scales given as a strided
+ * view (byte (r, b) at s[r * rs + b * bs], rs, bs >= 0) into the matrix-core
+ * scale layout described above (out: rows * blocks bytes, 4-byte aligned),
+ * so that scales held in a plain layout can feed the _mfma contractions.
+ * rows must be a multiple of 64 and blocks of 4.
+ * mx_scales_from_mfma -- the inverse: the flat matrix-core buffer `in` is
+ * written to the strided view s, whose positions must be distinct (rs, bs
+ * >= 1 and rs >= blocks * bs or bs >= rows * rs).
+ *
+ * Errors: MX_E_NULL, MX_E_SHAPE (negative, not multiples of 64 / 4, or above
+ * 2^30), MX_E_STRIDE (a negative or too large stride, or a written view that
+ * aliases itself), MX_E_ALIGN (flat buffer not 4-byte aligned),
+ * MX_E_OVERLAP.  rows == 0 or blocks == 0 is a no-op.
+ */
+int mx_scales_to_mfma(const uint8_t *s, int64_t rs, int64_t bs, int64_t rows, int64_t blocks, uint8_t *out,
+                      void *stream);
+int mx_scales_from_mfma(const uint8_t *in, int64_t rows, int64_t blocks, uint8_t *s, int64_t rs, int64_t bs,
+                        void *stream);
+
 /* Host function: a static, human-readable name for an mx_status value. */
 const char *mx_status_string(int status);
 

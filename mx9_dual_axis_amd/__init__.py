@@ -71,13 +71,16 @@ def _load():
     lib.mx_grouped_gemm_k.argtypes = [P, I64, P, I64, I64, P, I64, P, I64, I64, P, I32, I64, I64, I64, P, I64, I64,
                                       I32, P]
     lib.mx_gemm_nt_mfma.argtypes = [P, I64, P, P, I64, P, I64, I64, I64, P, I64, I32, P]
+    lib.mx_scales_to_mfma.argtypes = [P, I64, I64, I64, I64, P, P]
+    lib.mx_scales_from_mfma.argtypes = [P, I64, I64, P, I64, I64, P]
     lib.mx_grouped_gemm_rows_mfma.argtypes = [P, I64, P, P, I64, I64, P, I64, P, I32, I64, I64, I64, P, I64, I32, P]
     lib.mx_grouped_gemm_k_mfma.argtypes = [P, I64, P, P, I64, P, P, I32, I64, I64, I64, P, I64, I64, I32, P]
     for f in (lib.mx_quantize_2d_dual, lib.mx_quantize_grouped, lib.mx9_pack, lib.mx9_unpack,
               lib.mx9_pack_axis, lib.mx9_unpack_axis, lib.mx9_pack_records, lib.mx9_unpack_records,
               lib.mx_gemm_nt, lib.mx_grouped_gemm_rows, lib.mx_grouped_gemm_k,
               lib.mx_quantize_2d_dual_mfma, lib.mx_quantize_grouped_mfma, lib.mx_gemm_nt_mfma,
-              lib.mx_grouped_gemm_rows_mfma, lib.mx_grouped_gemm_k_mfma):
+              lib.mx_grouped_gemm_rows_mfma, lib.mx_grouped_gemm_k_mfma, lib.mx_scales_to_mfma,
+              lib.mx_scales_from_mfma):
         f.restype = ctypes.c_int
     lib.mx_status_string.argtypes = [ctypes.c_int]
     lib.mx_status_string.restype = ctypes.c_char_p
@@ -507,6 +510,37 @@ def mx_grouped_gemm_k_mfma(A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, s
                                           sB.data_ptr(), offs.data_ptr(), G, M, N, K, C.data_ptr(), C.stride(1),
                                           C.stride(0), _out_code(C.dtype), _stream(A.device)))
     return C
+
+
+def scales_to_mfma(s: torch.Tensor, out: torch.Tensor | None = None):
+    """Plain E8M0 scales s [rows, blocks] (any strides, uint8) -> a flat
+    uint8 [rows * blocks] buffer in the matrix-core scale layout."""
+    _need_cuda(s, "s")
+    if s.dtype != torch.uint8 or s.dim() != 2:
+        raise ValueError("s must be a 2-D uint8 view")
+    rows, blocks = s.shape
+    if out is None:
+        out = torch.empty((rows * blocks,), dtype=torch.uint8, device=s.device)
+    elif out.dtype != torch.uint8 or not out.is_contiguous() or out.numel() != rows * blocks:
+        raise ValueError("out must be a contiguous uint8 buffer of rows * blocks bytes")
+    _check(_load().mx_scales_to_mfma(s.data_ptr(), s.stride(0), s.stride(1), rows, blocks, out.data_ptr(),
+                                     _stream(s.device)))
+    return out
+
+
+def scales_from_mfma(flat: torch.Tensor, rows: int, blocks: int, out: torch.Tensor | None = None):
+    """Inverse of scales_to_mfma: a flat matrix-core buffer -> plain
+    [rows, blocks] (out may be any non-aliasing strided view)."""
+    _need_cuda(flat, "flat")
+    if flat.dtype != torch.uint8 or not flat.is_contiguous() or flat.numel() != rows * blocks:
+        raise ValueError("flat must be a contiguous uint8 buffer of rows * blocks bytes")
+    if out is None:
+        out = torch.empty((rows, blocks), dtype=torch.uint8, device=flat.device)
+    elif out.dtype != torch.uint8 or tuple(out.shape) != (rows, blocks):
+        raise ValueError("out must be a uint8 [rows, blocks] view")
+    _check(_load().mx_scales_from_mfma(flat.data_ptr(), rows, blocks, out.data_ptr(), out.stride(0), out.stride(1),
+                                       _stream(flat.device)))
+    return out
 
 
 # --- the pages' call signatures ------------------------------------------

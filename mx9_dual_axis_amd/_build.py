@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxq.so")
-SOURCES = ["dual_axis.hip", "mx9.hip", "mx9_layouts.hip", "mx_gemm.hip", "mxq_abi.cpp"]
+SOURCES = ["dual_axis.hip", "mx9.hip", "mx9_layouts.hip", "mx_gemm.hip", "scale_layout.hip", "mxq_abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

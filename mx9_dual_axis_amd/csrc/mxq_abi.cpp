@@ -214,6 +214,26 @@ int gemm_k_call(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs,
     return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
 }
 
+// Checks of the scale-layout conversions: view (rs, bs) of rows x blocks
+// plain scales, flat buffer of rows * blocks bytes in the matrix-core layout.
+// A view that is written (the inverse conversion) must not alias itself.
+int check_scale_conversion(const uint8_t* view, int64_t rs, int64_t bs, int64_t rows, int64_t blocks,
+                           const uint8_t* flat, bool view_written) {
+    const bool empty = rows == 0 || blocks == 0;
+    if (!empty && (!view || !flat)) return MX_E_NULL;
+    if (rows < 0 || blocks < 0 || rows % 64 != 0 || blocks % 4 != 0 || rows > kMaxDim || blocks > kMaxDim)
+        return MX_E_SHAPE;
+    if (uint64_t(rows) * uint64_t(blocks) / 4 > kMaxThreads) return MX_E_SHAPE;
+    if (rs < 0 || bs < 0 || rs > kMaxDim || bs > kMaxDim) return MX_E_STRIDE;
+    if (view_written && !empty &&
+        !(rs >= 1 && bs >= 1 && (rs >= blocks * bs || bs >= rows * rs)))
+        return MX_E_STRIDE;
+    if (!empty && !aligned(flat, 4)) return MX_E_ALIGN;
+    const Span a{addr(view), scale_span(rows, blocks, rs, bs)}, b{addr(flat), empty ? 0u : uint64_t(rows * blocks)};
+    if (overlap(a, b)) return MX_E_OVERLAP;
+    return MX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -427,6 +447,24 @@ int mx_grouped_gemm_k_mfma(const uint8_t* A, int64_t lda, const uint8_t* sA, con
                            const uint8_t* sB, const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
                            void* C, int64_t ldc, int64_t c_gs, int32_t out_dtype, void* stream) {
     return gemm_k_call(A, lda, sA, 0, 0, B, ldb, sB, 0, 0, offs, G, M, N, K, C, ldc, c_gs, out_dtype, true, stream);
+}
+
+int mx_scales_to_mfma(const uint8_t* s, int64_t rs, int64_t bs, int64_t rows, int64_t blocks, uint8_t* out,
+                      void* stream) {
+    int rc = check_scale_conversion(s, rs, bs, rows, blocks, out, false);
+    if (rc != MX_OK) return rc;
+    if (rows == 0 || blocks == 0) return MX_OK;
+    hipError_t e = mxq::launch_scales_to_mfma(s, rs, bs, rows, blocks, out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
+}
+
+int mx_scales_from_mfma(const uint8_t* in, int64_t rows, int64_t blocks, uint8_t* s, int64_t rs, int64_t bs,
+                        void* stream) {
+    int rc = check_scale_conversion(s, rs, bs, rows, blocks, in, true);
+    if (rc != MX_OK) return rc;
+    if (rows == 0 || blocks == 0) return MX_OK;
+    hipError_t e = mxq::launch_scales_from_mfma(in, rows, blocks, s, rs, bs, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
 }
 
 }  // extern "C"

@@ -56,4 +56,9 @@ hipError_t launch_mx_gemm(const uint8_t* A, int64_t lda, const uint8_t* sA, int6
                           int64_t K, const int32_t* offs, int32_t G, int mode, int out_dtype, bool mfma_scales,
                           hipStream_t stream);
 
+hipError_t launch_scales_to_mfma(const uint8_t* s, int64_t rs, int64_t bs, int64_t rows, int64_t blocks, uint8_t* out,
+                                 hipStream_t stream);
+hipError_t launch_scales_from_mfma(const uint8_t* in, int64_t rows, int64_t blocks, uint8_t* s, int64_t rs, int64_t bs,
+                                   hipStream_t stream);
+
 }  // namespace mxq

@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
                                   "mx9_pack_axis", "mx9_unpack_axis", "mx9_pack_records", "mx9_unpack_records",
                                   "mx_gemm_nt", "mx_grouped_gemm_rows", "mx_grouped_gemm_k", "mx_status_string",
                                   "mx_quantize_2d_dual_mfma", "mx_quantize_grouped_mfma", "mx_gemm_nt_mfma",
-                                  "mx_grouped_gemm_rows_mfma", "mx_grouped_gemm_k_mfma"])
+                                  "mx_grouped_gemm_rows_mfma", "mx_grouped_gemm_k_mfma", "mx_scales_to_mfma",
+                                  "mx_scales_from_mfma"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -194,6 +195,22 @@ def test_matrix_core_layout_validation_codes():
                                          128, 128, 256, FAKE * 5, 128, 0, None) == 1
     assert lib.mx_grouped_gemm_k_mfma(FAKE, 256, FAKE * 2, FAKE * 3, 256, FAKE * 4, FAKE * 6, 4, 128, 128, 256,
                                       FAKE * 5, 128, 128 * 127, 0, None) == 6
+
+
+def test_scale_conversion_validation_codes():
+    lib = mxq.library()
+
+    def to(s=FAKE, rs=16, bs=1, rows=128, blocks=16, out=FAKE * 2):
+        return lib.mx_scales_to_mfma(s, rs, bs, rows, blocks, out, None)
+
+    def frm(flat=FAKE * 2, rows=128, blocks=16, s=FAKE, rs=16, bs=1):
+        return lib.mx_scales_from_mfma(flat, rows, blocks, s, rs, bs, None)
+    assert to(s=None) == 1 and frm(flat=None) == 1
+    assert to(rows=96) == 5 and to(blocks=6) == 5 and frm(rows=-64) == 5
+    assert to(rs=-1) == 6 and frm(rs=0) == 6 and frm(rs=8) == 6          # a written view must not alias
+    assert to(out=FAKE * 2 + 2) == 7
+    assert to(out=FAKE + 1024) == 8 and frm(flat=FAKE + 64) == 8
+    assert to(rows=0, s=None, out=None) == 0 and frm(blocks=0, s=None, flat=None) == 0
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch):

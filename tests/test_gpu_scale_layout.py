@@ -404,3 +404,51 @@ def test_pipeline_edge_cases():
     ref, absC = oracle.mx_grouped_gemm_rows(A2, sA2, Bw, sBw, offs2, sa_strides=(8, 1), sb_strides=(8, 1),
                                             threads=THREADS, with_abs=True)
     _assert_close(Y, ref, absC, 256, torch.float32, "two-step row groups")
+
+
+@pytest.mark.parametrize("R,kb,view", [(64, 4, "rows"), (256, 160, "rows"), (384, 12, "transposed"),
+                                       (128, 8, "pitched")])
+def test_scale_conversions(R, kb, view):
+    """mx_scales_to_mfma / mx_scales_from_mfma: the oracle's index function,
+    from and to row-major, transposed (the colwise cast's s_col read as its
+    operand's scales) and pitched views."""
+    dev = require_gpu()
+    say(f"scale layout conversion R={R} kb={kb} view={view}")
+    g = np.random.default_rng(R + kb)
+    S = g.integers(0, 256, (R, kb), dtype=np.uint8)
+    want = oracle.scales_to_mfma(S)
+    if view == "rows":
+        src = _dev(S)
+    elif view == "transposed":
+        src = _dev(np.ascontiguousarray(S.T)).t()
+    else:
+        wide = torch.zeros((R, kb + 12), dtype=torch.uint8, device=dev)
+        wide[:, :kb] = _dev(S)
+        src = wide[:, :kb]
+    flat = mxq.scales_to_mfma(src)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(flat), want)
+    back = torch.full((kb, R), 0xEE, dtype=torch.uint8, device=dev).t() if view == "transposed" else None
+    back = mxq.scales_from_mfma(flat, R, kb, out=back)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(back.contiguous()), S)
+
+
+def test_converted_plain_scales_feed_the_fast_contraction():
+    """The plain-layout cast, its scales converted, the pipelined contraction:
+    the same result as the strided-view contraction on the plain scales."""
+    dev = require_gpu()
+    say("plain cast -> converted scales -> pipelined contraction")
+    M, K, N = 512, 768, 256
+    xd = bf16_to_dev(synth.normal_bf16(M, K, 51))
+    q_row, s_row, q_col, s_col = mxq.mx_quantize_2d_dual(xd)
+    g = np.random.default_rng(52)
+    W = _codes(g, (N, K))
+    sW = g.integers(118, 137, (N, K // 32), dtype=np.uint8)
+    C1 = mxq.mx_gemm_nt(q_row, s_row, _dev(W), _dev(sW))
+    C2 = mxq.mx_gemm_nt_mfma(q_row, mxq.scales_to_mfma(s_row), _dev(W), mxq.scales_to_mfma(_dev(sW)))
+    # weight gradient operand: q_col [K, M] with s_col [M/32, K] read transposed
+    G1 = mxq.mx_gemm_nt(q_col, s_col.t(), q_col, s_col.t())
+    G2 = mxq.mx_gemm_nt_mfma(q_col, mxq.scales_to_mfma(s_col.t()), q_col, mxq.scales_to_mfma(s_col.t()))
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2) and torch.equal(G1, G2)

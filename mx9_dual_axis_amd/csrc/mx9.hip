@@ -13,10 +13,12 @@
 // exponent maximum and prime bits are combined with DPP.  Strided or ragged
 // inputs take one thread per block.  bf16 inputs are widened exactly to fp32
 // bit patterns (bf16 is the upper half of binary32), so one code path serves
-// both input types.  The quotient x / 2^(E-6-p) is formed with v_ldexp_f32,
-// exact because the divisor is a power of two and |quotient| < 2^8, then
-// rounded half-to-even by v_rndne_f32; fp32 denormals are kept (no flush),
-// so subnormal inputs quantize exactly.
+// both input types.  The quotient x / 2^(E-6-p) is rounded half-to-even
+// in one fused multiply-add with 1.5 * 2^23 (its reciprocal is a normal
+// float for every block whose exponent byte is at least 9; smaller blocks
+// form it exactly with v_ldexp_f32), and clamped with one median.  A wave
+// issues one 16-byte load per lane: four loads per lane before computing
+// measured no faster in the cast -> pack -> unpack sequence on MI355X.
 //
 // Cache policy of the flat kernels (each byte is touched once): the pack
 // reads its input and writes q, max_exp and prime with the non-temporal

@@ -37,24 +37,56 @@ __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, ui
     return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
 }
 
+// round-half-even(x * scale) clamped to [-127, 127] in the low byte, for a
+// power-of-two scale.  The fused multiply-add forms x * scale + 1.5 * 2^23
+// exactly and rounds it once; |x * scale| < 2^8, so the sum lies in
+// [2^23, 2^24), where floats are the integers, and the rounding is the
+// half-even rounding of x * scale (1.5 * 2^23 is even).  The median then
+// clamps the integer to 1.5 * 2^23 +- 127.
+__device__ __forceinline__ uint32_t qbits_scaled(uint32_t w, float scale) {
+    const float t = __builtin_fmaf(__uint_as_float(w), scale, 12582912.0f);
+    return __float_as_uint(__builtin_amdgcn_fmed3f(t, 12582785.0f, 12583039.0f));
+}
+
 // Quantize pairs of fp32 patterns against the block's shared exponent byte S.
 // A pair is demoted (p = 1) when its larger magnitude is below 2^(S-127),
 // i.e. when its larger magnitude pattern is below S << 23 (magnitudes and
 // their bit patterns order alike).  Returns the q bytes of kPairs pairs in
 // kPairs / 2 dwords and the pair bits in *bits (LSB = first pair).
+//
+// The grid's reciprocal is 2^(133 + p - S).  For S >= 9 it is a normal float
+// (at most 2^125) and the quantization is one fused multiply-add and one
+// median per element; an element below the smallest normal then has
+// |x * scale| < 1/2 and rounds to 0 whether or not the hardware keeps it
+// subnormal.  Blocks with S < 9 (largest magnitude below 2^-118) take the
+// exact ldexp route.
 template <int kPairs>
 __device__ __forceinline__ void quantize_pairs(const uint32_t (&w)[2 * kPairs], uint32_t S,
                                                uint32_t (&qd)[kPairs / 2], uint32_t& bits) {
     uint32_t qb[2 * kPairs];
     bits = 0;
+    const uint32_t thr = S << 23;
+    if (S >= 9u) {
+        const uint32_t base = (260u - S) << 23;        // 2^(133 - S) as a float pattern
 #pragma unroll
-    for (int j = 0; j < kPairs; ++j) {
-        const uint32_t pm = max(w[2 * j] & 0x7FFFFFFFu, w[2 * j + 1] & 0x7FFFFFFFu);
-        const uint32_t p = pm < (S << 23) ? 1u : 0u;
-        bits |= p << j;
-        const int shift = 133 + int(p) - int(S);          // 6 + p - E, E = S - 127
-        qb[2 * j] = qbits(w[2 * j], shift);
-        qb[2 * j + 1] = qbits(w[2 * j + 1], shift);
+        for (int j = 0; j < kPairs; ++j) {
+            const uint32_t pm = max(w[2 * j] & 0x7FFFFFFFu, w[2 * j + 1] & 0x7FFFFFFFu);
+            const uint32_t p = (pm - thr) >> 31;        // pm < thr; both are below 2^31
+            bits |= p << j;
+            const float scale = __uint_as_float(base + (p << 23));
+            qb[2 * j] = qbits_scaled(w[2 * j], scale);
+            qb[2 * j + 1] = qbits_scaled(w[2 * j + 1], scale);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kPairs; ++j) {
+            const uint32_t pm = max(w[2 * j] & 0x7FFFFFFFu, w[2 * j + 1] & 0x7FFFFFFFu);
+            const uint32_t p = pm < thr ? 1u : 0u;
+            bits |= p << j;
+            const int shift = 133 + int(p) - int(S);      // 6 + p - E, E = S - 127
+            qb[2 * j] = qbits(w[2 * j], shift);
+            qb[2 * j + 1] = qbits(w[2 * j + 1], shift);
+        }
     }
 #pragma unroll
     for (int k = 0; k < kPairs / 2; ++k) qd[k] = pack4(qb[4 * k], qb[4 * k + 1], qb[4 * k + 2], qb[4 * k + 3]);

@@ -308,6 +308,26 @@ __device__ __forceinline__ typename Raw<kDtype, kPer>::type load_raw(const void*
     }
 }
 
+#if defined(__HIP_DEVICE_COMPILE__)
+// The same load through a buffer resource: byte offset voff (per lane) plus
+// soff (wave-uniform, a scalar register), so a batch of rows costs no vector
+// address arithmetic.  The resource never clips (num_records is 2^32 - 1);
+// callers keep every offset inside the tensor.
+template <int kDtype, int kPer>
+__device__ __forceinline__ typename Raw<kDtype, kPer>::type load_raw_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                                         uint32_t soff) {
+    constexpr int kNt = 2;   // the non-temporal hint
+    if constexpr (kDtype == 0 && kPer == 2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, int(voff), int(soff), kNt);
+        return make_uint2(v[0], v[1]);
+    } else if constexpr (kDtype == 1 && kPer == 1) {
+        return uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, int(voff), int(soff), kNt)) << 16;
+    } else {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, int(voff), int(soff), kNt);
+    }
+}
+#endif
+
 template <int kDtype, int kPer>
 __device__ __forceinline__ uint32_t raw_elem(typename Raw<kDtype, kPer>::type r, int e) {
     if constexpr (kDtype == 0 && kPer == 2) {
@@ -346,13 +366,17 @@ void mx9_pack_axis_tile(const void* __restrict__ xv, AxisTiles v, int8_t* __rest
     __shared__ uint4 lds[T::kLds / 16];
     uint8_t* ls = reinterpret_cast<uint8_t*>(lds);
     const TileCoord c = tile_coord<kPer>(v);
-    const uint32_t il = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const uint32_t il = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t r0 = il * kPer;                  // the lane's first row in the tile
     const bool live_i = r0 < c.rows;                // kPer == 2: rows come in pairs (inner is even)
     const uint64_t i = c.i0 + r0;
-    // Batches of kU blocks: every load of a batch is issued (predicated, not
-    // branched) before any of its blocks is computed, so 16 * kU loads per
-    // lane are in flight.
+    constexpr uint32_t kEsz = kDtype == 0 ? 4u : 2u;
+    // The offsets of a batch (64 element rows) fit 32 bits when an element
+    // row is below 2^26 bytes; longer rows take the general route below.
+    const bool small_row = v.inner * kEsz < (uint64_t(1) << 26);
+    // Batches of kU blocks: every load of a batch is issued before any of its
+    // blocks is computed, so 16 * kU loads per lane are in flight.
     using RawT = typename Raw<kDtype, kPer>::type;
     constexpr int kU = 4;
     static_assert(T::kJW % kU == 0, "batches divide the wave's blocks");
@@ -361,15 +385,38 @@ void mx9_pack_axis_tile(const void* __restrict__ xv, AxisTiles v, int8_t* __rest
         const uint32_t jl0 = wave * T::kJW + uint32_t(b0);
         if (jl0 >= c.nj) break;                     // uniform across the wave
         RawT raw[kU][16];
+        const int64_t l_first = int64_t(16) * (c.j0 + jl0);
+        if (small_row && jl0 + kU <= c.nj && l_first + 16 * kU <= v.len) {
+            // Every row of the batch exists: a load's address is the batch's
+            // first row (wave-uniform) plus the row's offset (wave-uniform)
+            // plus the lane's position, and no load is predicated.  Lanes past
+            // the tile's live rows read position i0 (which exists); their
+            // results are never written out.
+#if defined(__HIP_DEVICE_COMPILE__)
+            const uint32_t voff = uint32_t(live_i ? i : c.i0) * kEsz;
+            const char* rows = static_cast<const char*>(xv) +
+                               (c.o * uint64_t(v.len) + uint64_t(l_first)) * v.inner * kEsz;
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rows), 0, int(0xFFFFFFFFu), 0x00020000);
+            const uint32_t pitch = uint32_t(v.inner) * kEsz;
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const int64_t l0 = int64_t(16) * (c.j0 + jl0 + u);
+            for (int u = 0; u < kU; ++u) {
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const int64_t l = l0 + k;
-                raw[u][k] = RawT{};
-                if (live_i && jl0 + u < c.nj && l < v.len)
-                    raw[u][k] = load_raw<kDtype, kPer>(xv, (c.o * uint64_t(v.len) + uint64_t(l)) * v.inner + i);
+                for (int k = 0; k < 16; ++k)
+                    raw[u][k] = load_raw_buf<kDtype, kPer>(rs, voff, uint32_t(16 * u + k) * pitch);
+            }
+#endif
+        } else {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int64_t l0 = l_first + 16 * u;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const int64_t l = l0 + k;
+                    raw[u][k] = RawT{};
+                    if (live_i && jl0 + u < c.nj && l < v.len)
+                        raw[u][k] = load_raw<kDtype, kPer>(xv, (c.o * uint64_t(v.len) + uint64_t(l)) * v.inner + i);
+                }
             }
         }
 #pragma unroll

@@ -80,6 +80,15 @@ def test_special_values_and_subnormals():
     bits[4, :16] = 0x7F7FFFFF                                 # fp32 max
     bits[5, :16] = [0x3FFF0000, 0x3F810000, 0x3F830000, 0x3F7F8000] * 4   # clamp and ties
     bits[6, :] = (g.integers(1, 255, 256) << 23) | g.integers(0, 1 << 23, 256)  # all binades
+    # blocks whose exponent byte runs 3..18 (either side of where the float
+    # scale replaces ldexp), partnered with subnormals and the smallest
+    # normals, some of which round to +-1 or sit on ties
+    for t in range(16):
+        blk = bits[7, 16 * t:16 * t + 16]
+        blk[:] = (g.integers(0, 2, 16) << 23) | g.integers(0, 1 << 23, 16)
+        blk[0] = ((3 + t) << 23) | int(g.integers(0, 1 << 23))
+        blk[1 + t % 15] = (1 << 22) if t % 2 else (3 << 21)
+        blk[:] |= (g.integers(0, 2, 16) << 31).astype(np.uint32)
     q, e, p, _ = _check_pack(x, "specials fp32")
     _check_unpack(q, e, p, 64, 256, "specials", "fp32")
     _check_unpack(q, e, p, 64, 256, "specials", "bf16")

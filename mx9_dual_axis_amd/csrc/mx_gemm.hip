@@ -249,6 +249,43 @@ void mx_gemm_kernel(GemmArgs p) {
 }
 
 
+// Scale forms of the pipelined kernel.  kScalesMfma: 64-row groups of
+// 256-byte runs in the matrix-core layout.  kScalesRows: plain scales with
+// the blocks of a row adjacent (block stride 1, row stride a multiple of 4),
+// as the rowwise cast writes them.  kScalesBlocks: plain scales with the rows
+// of a block adjacent (row stride 1, block stride a multiple of 4), as the
+// colwise cast's s_col read through its transpose.  A plain run is the 64
+// rows x 4 blocks of one contraction step, loaded as 64 dwords (one row's 4
+// blocks, or 4 rows of one block) and gathered into the matrix-core dword at
+// read time (four byte reads).
+constexpr int kScalesMfma = 0, kScalesRows = 1, kScalesBlocks = 2;
+
+// A plain run's contribution to a lane's scale dword: byte q of the dword is
+// the scale of run row 16 q + lane % 16, block lane / 16.  The four bytes lie
+// in four dwords at a fixed stride (64 bytes in the rows form, 16 in the
+// blocks form), read as two pairs; plain_scale_pick then takes the lane's
+// byte of each with byte permutes.
+template <int kSF>
+__device__ __forceinline__ void plain_scale_read(const uint8_t* run, uint32_t lane, uint32_t (&raw)[4]) {
+    constexpr uint32_t kStride = kSF == kScalesRows ? 16u : 4u;   // dwords
+    const uint32_t* d = reinterpret_cast<const uint32_t*>(run) +
+                        (kSF == kScalesRows ? (lane & 15u) : 16u * (lane >> 4) + ((lane & 15u) >> 2));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) raw[q] = d[q * kStride];
+}
+
+template <int kSF>
+__device__ __forceinline__ uint32_t plain_scale_sel(uint32_t lane) {
+    const uint32_t b = kSF == kScalesRows ? (lane >> 4) : (lane & 3u);    // byte within each dword
+    return b | ((4u + b) << 8) | 0x0C0C0000u;
+}
+
+__device__ __forceinline__ int plain_scale_pick(const uint32_t (&raw)[4], uint32_t sel) {
+    const uint32_t lo = __builtin_amdgcn_perm(raw[1], raw[0], sel);
+    const uint32_t hi = __builtin_amdgcn_perm(raw[3], raw[2], sel);
+    return int(__builtin_amdgcn_perm(hi, lo, 0x05040100u));
+}
+
 // acc[i][J] += a[i] x b for every i (J, the column sub-tile, is fixed).
 template <int J, int MS, int NS, int... I>
 __device__ __forceinline__ void mma_col(v4f (&acc)[MS][NS], const v8i (&a)[MS], const v8i& b, const int (&sa)[MS / 4],
@@ -300,6 +337,34 @@ __device__ __forceinline__ void mma_step(v4f (&acc)[MS][NS], const uint4* sa_lds
         a[i] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
     }
     v8i b = b_frag<0>(sb_lds, b_row0, lane);
+    (mma_b<J>(acc, a, b, sb_lds, b_row0, lane, sa, sb), ...);
+}
+
+// The same step with plain-form scales: their raw dwords were read before
+// this step's fragments, and are combined only after every fragment read of
+// the step's first column is issued, so that the combining waits for the
+// scale reads alone.
+template <int MS, int NS, int... J>
+__device__ __forceinline__ void mma_step_plain(v4f (&acc)[MS][NS], const uint4* sa_lds, const uint4* sb_lds,
+                                               uint32_t a_row0, uint32_t b_row0, uint32_t lane,
+                                               const uint32_t (&ra)[MS / 4][4], const uint32_t (&rb)[NS / 4][4],
+                                               uint32_t sel, std::integer_sequence<int, J...>) {
+    const uint32_t g = lane >> 4, sw = lane & 7u;
+    v8i a[MS];
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+        const uint32_t r = a_row0 + 16u * i + (lane & 15u);
+        const uint4 lo = sa_lds[r * 8u + (g ^ sw)];
+        const uint4 hi = sa_lds[r * 8u + ((4u + g) ^ sw)];
+        a[i] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+    }
+    v8i b = b_frag<0>(sb_lds, b_row0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    int sa[MS / 4], sb[NS / 4];
+#pragma unroll
+    for (int j = 0; j < MS / 4; ++j) sa[j] = plain_scale_pick(ra[j], sel);
+#pragma unroll
+    for (int j = 0; j < NS / 4; ++j) sb[j] = plain_scale_pick(rb[j], sel);
     (mma_b<J>(acc, a, b, sb_lds, b_row0, lane, sa, sb), ...);
 }
 
@@ -383,7 +448,7 @@ struct Pipe {
     static_assert(kStages == 2 || kLoads < 16, "vmcnt immediate");
 };
 
-template <int kOut, int MS, int NS, int WM, int WN>
+template <int kOut, int MS, int NS, int WM, int WN, int kSF>
 __global__ __launch_bounds__(64 * WM * WN, WM * WN >= 8 ? 2 : 1)
 void mx_gemm_pipe_kernel(GemmArgs p) {
     using P = Pipe<MS, NS, WM, WN>;
@@ -447,18 +512,30 @@ void mx_gemm_pipe_kernel(GemmArgs p) {
     // scale runs of this wave (A groups first, then B groups; groups past a
     // ragged last tile clamp to the last one; runs past the last repeat it)
     const int64_t ga_max = p.M / 64 - 1 - m0 / 64, gb_max = p.N / 64 - 1 - n0 / 64;
-    const v4i rs_a = pipe_rsrc(p.sA + (m0 / 64) * p.sa_rs);
-    const v4i rs_b = pipe_rsrc(sB + (n0 / 64) * p.sb_rs);
+    // the scales of the tile's first row, and per run: the run's offset from
+    // there, the offset added per contraction step and the lane's offset
+    const int64_t a_org = kSF == kScalesMfma ? (m0 / 64) * p.sa_rs : kSF == kScalesRows ? m0 * p.sa_rs : m0;
+    const int64_t b_org = kSF == kScalesMfma ? (n0 / 64) * p.sb_rs : kSF == kScalesRows ? n0 * p.sb_rs : n0;
+    const v4i rs_a = pipe_rsrc(p.sA + a_org);
+    const v4i rs_b = pipe_rsrc(sB + b_org);
     bool run_a[P::kRpw];
-    uint32_t s_run_off[P::kRpw];
+    uint32_t s_run_off[P::kRpw], s_step[P::kRpw], v_run[P::kRpw];
 #pragma unroll
     for (int r = 0; r < P::kRpw; ++r) {
         const uint32_t run = min(wave * uint32_t(P::kRpw) + uint32_t(r), uint32_t(P::kRuns - 1));
         run_a[r] = run < uint32_t(P::kRunsA);
-        s_run_off[r] = run_a[r] ? uint32_t(min(int64_t(run), ga_max)) * uint32_t(p.sa_rs)
-                                : uint32_t(min(int64_t(run - P::kRunsA), gb_max)) * uint32_t(p.sb_rs);
+        const uint32_t g = run_a[r] ? uint32_t(min(int64_t(run), ga_max)) : uint32_t(min(int64_t(run - P::kRunsA), gb_max));
+        const uint32_t rs = uint32_t(run_a[r] ? p.sa_rs : p.sb_rs), bs = uint32_t(run_a[r] ? p.sa_bs : p.sb_bs);
+        if constexpr (kSF == kScalesMfma) {
+            s_run_off[r] = g * rs; s_step[r] = 256u; v_run[r] = 4u * lane;
+        } else if constexpr (kSF == kScalesRows) {
+            s_run_off[r] = 64u * g * rs; s_step[r] = 4u; v_run[r] = lane * rs;
+        } else {
+            s_run_off[r] = 64u * g; s_step[r] = 4u * bs; v_run[r] = (lane >> 4) * bs + 4u * (lane & 15u);
+        }
     }
     const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(lds));
+    const uint32_t plain_sel = plain_scale_sel<kSF == kScalesMfma ? kScalesRows : kSF>(lane);
 #define MXQ_PIPE_ISSUE(step)                                                                     \
     do {                                                                                         \
         const uint32_t k_ = uint32_t(k_lo + int64_t(step) * kTile);                              \
@@ -472,8 +549,8 @@ void mx_gemm_pipe_kernel(GemmArgs p) {
             pipe_load16(rb, st_ + P::kB + 1024u * j_, vob, ((8u * j_) & b_mask) * ldb + k_);     \
         }                                                                                        \
         _Pragma("unroll") for (int r_ = 0; r_ < P::kRpw; ++r_)                                   \
-            pipe_load4(run_a[r_] ? rs_a : rs_b, st_ + P::kS + 256u * (wave * P::kRpw + r_), 4u * lane, \
-                       s_run_off[r_] + (k_ / uint32_t(kTile)) * 256u);                           \
+            pipe_load4(run_a[r_] ? rs_a : rs_b, st_ + P::kS + 256u * (wave * P::kRpw + r_), v_run[r_], \
+                       s_run_off[r_] + (k_ / uint32_t(kTile)) * s_step[r_]);                      \
     } while (0)
 
     v4f acc[MS][NS];
@@ -496,15 +573,28 @@ void mx_gemm_pipe_kernel(GemmArgs p) {
         }
         if (s + P::kStages - 1 < n) MXQ_PIPE_ISSUE(s + P::kStages - 1);
         const uint8_t* st = lds + uint32_t(s % P::kStages) * P::kStage;
-        int sa[MS / 4], sb[NS / 4];
+        const uint8_t* runs_a = st + P::kS + 256u * ((MS / 4) * wm);
+        const uint8_t* runs_b = st + P::kS + 256u * (P::kRunsA + (NS / 4) * wn);
+        if constexpr (kSF == kScalesMfma) {
+            int sa[MS / 4], sb[NS / 4];
 #pragma unroll
-        for (int j = 0; j < MS / 4; ++j)
-            sa[j] = *reinterpret_cast<const int*>(st + P::kS + 256u * ((MS / 4) * wm + j) + 4u * lane);
+            for (int j = 0; j < MS / 4; ++j) sa[j] = *reinterpret_cast<const int*>(runs_a + 256u * j + 4u * lane);
 #pragma unroll
-        for (int j = 0; j < NS / 4; ++j)
-            sb[j] = *reinterpret_cast<const int*>(st + P::kS + 256u * (P::kRunsA + (NS / 4) * wn + j) + 4u * lane);
-        mma_step<MS, NS>(acc, reinterpret_cast<const uint4*>(st + P::kA), reinterpret_cast<const uint4*>(st + P::kB),
-                         wm * 16u * MS, wn * 16u * NS, lane, sa, sb, std::make_integer_sequence<int, NS>{});
+            for (int j = 0; j < NS / 4; ++j) sb[j] = *reinterpret_cast<const int*>(runs_b + 256u * j + 4u * lane);
+            mma_step<MS, NS>(acc, reinterpret_cast<const uint4*>(st + P::kA),
+                             reinterpret_cast<const uint4*>(st + P::kB), wm * 16u * MS, wn * 16u * NS, lane, sa, sb,
+                             std::make_integer_sequence<int, NS>{});
+        } else {
+            uint32_t ra[MS / 4][4], rb[NS / 4][4];
+#pragma unroll
+            for (int j = 0; j < MS / 4; ++j) plain_scale_read<kSF>(runs_a + 256u * j, lane, ra[j]);
+#pragma unroll
+            for (int j = 0; j < NS / 4; ++j) plain_scale_read<kSF>(runs_b + 256u * j, lane, rb[j]);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_step_plain<MS, NS>(acc, reinterpret_cast<const uint4*>(st + P::kA),
+                                   reinterpret_cast<const uint4*>(st + P::kB), wm * 16u * MS, wn * 16u * NS, lane,
+                                   ra, rb, plain_sel, std::make_integer_sequence<int, NS>{});
+        }
     }
 #undef MXQ_PIPE_ISSUE
     __syncthreads();
@@ -546,6 +636,38 @@ void mx_gemm_pipe_kernel(GemmArgs p) {
     }
 }
 
+// The plain scale form a view allows the pipelined kernel to load, or -1:
+// rows form (block stride 1, row stride a multiple of 4), blocks form (row
+// stride 1, block stride a multiple of 4); the base and the per-group stride
+// keep every dword 4-byte aligned, and every offset fits 31 bits.
+int plain_scale_form(const uint8_t* s, int64_t rs, int64_t bs, int64_t K, int64_t gs) {
+    if (reinterpret_cast<uintptr_t>(s) % 4 != 0 || gs % 4 != 0) return -1;
+    if (bs == 1 && rs > 0 && rs % 4 == 0 && rs < (int64_t(1) << 24)) return kScalesRows;
+    if (rs == 1 && bs > 0 && bs % 4 == 0 && (K / 32 + 4) * bs < (int64_t(1) << 31)) return kScalesBlocks;
+    return -1;
+}
+
+// Row groups: 128-row tiles (one group unit) of 8 waves; otherwise 256 x 256.
+template <int kSF>
+hipError_t launch_pipe(GemmArgs& p, int out_dtype, hipStream_t stream) {
+    if (p.mode == 0 && p.offs != nullptr) {
+        using P = Pipe<4, 4, 2, 4>;
+        p.tiles_m = uint32_t(p.M / P::kTM);
+        p.tiles_n = uint32_t((p.N + P::kTN - 1) / P::kTN);
+        const dim3 grid(p.tiles_m * p.tiles_n), block(P::kThreads);
+        if (out_dtype == 0) hipLaunchKernelGGL((mx_gemm_pipe_kernel<0, 4, 4, 2, 4, kSF>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((mx_gemm_pipe_kernel<1, 4, 4, 2, 4, kSF>), grid, block, 0, stream, p);
+    } else {
+        using P = Pipe<4, 8, 4, 2>;
+        p.tiles_m = uint32_t((p.M + P::kTM - 1) / P::kTM);
+        p.tiles_n = uint32_t((p.N + P::kTN - 1) / P::kTN);
+        const dim3 grid(p.tiles_m * p.tiles_n * uint32_t(p.mode == 1 ? p.G : 1)), block(P::kThreads);
+        if (out_dtype == 0) hipLaunchKernelGGL((mx_gemm_pipe_kernel<0, 4, 8, 4, 2, kSF>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((mx_gemm_pipe_kernel<1, 4, 8, 4, 2, kSF>), grid, block, 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_mx_gemm(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, int64_t sa_bs,
@@ -563,29 +685,22 @@ hipError_t launch_mx_gemm(const uint8_t* A, int64_t lda, const uint8_t* sA, int6
         p.sa_rs = p.sb_rs = 2 * K;
         p.sa_bs = p.sb_bs = 0;
     }
-    // the matrix-core-layout form stores 16-byte pieces of C rows
+    // the pipelined kernel stores 16-byte pieces of C rows, and loads plain
+    // scales as dwords of one row's 4 blocks or of one block's 4 rows
     const int64_t esz = out_dtype == 0 ? 4 : 2;
     const bool rows16 = (reinterpret_cast<uintptr_t>(C) % 16 == 0) && (ldc * esz) % 16 == 0 &&
                         (mode != 1 || (c_gs * esz) % 16 == 0);
-    if (mfma_scales && rows16) {
-        // row groups: 128-row tiles (one group unit); otherwise 256 x 256
+    int sf = kScalesMfma;
+    if (!mfma_scales) {
         const bool row_groups = mode == 0 && offs != nullptr;
-        if (row_groups) {
-            using P = Pipe<4, 4, 2, 4>;
-            p.tiles_m = uint32_t(M / P::kTM);
-            p.tiles_n = uint32_t((N + P::kTN - 1) / P::kTN);
-            const dim3 grid(p.tiles_m * p.tiles_n), block(P::kThreads);
-            if (out_dtype == 0) hipLaunchKernelGGL((mx_gemm_pipe_kernel<0, 4, 4, 2, 4>), grid, block, 0, stream, p);
-            else hipLaunchKernelGGL((mx_gemm_pipe_kernel<1, 4, 4, 2, 4>), grid, block, 0, stream, p);
-        } else {
-            using P = Pipe<4, 8, 4, 2>;
-            p.tiles_m = uint32_t((M + P::kTM - 1) / P::kTM);
-            p.tiles_n = uint32_t((N + P::kTN - 1) / P::kTN);
-            const dim3 grid(p.tiles_m * p.tiles_n * uint32_t(mode == 1 ? G : 1)), block(P::kThreads);
-            if (out_dtype == 0) hipLaunchKernelGGL((mx_gemm_pipe_kernel<0, 4, 8, 4, 2>), grid, block, 0, stream, p);
-            else hipLaunchKernelGGL((mx_gemm_pipe_kernel<1, 4, 8, 4, 2>), grid, block, 0, stream, p);
-        }
-        return hipGetLastError();
+        const int fa = plain_scale_form(sA, sa_rs, sa_bs, K, 0);
+        const int fb = plain_scale_form(sB, sb_rs, sb_bs, K, row_groups ? sb_gs : 0);
+        sf = fa == fb ? fa : -1;
+    }
+    if (sf >= 0 && rows16) {
+        if (sf == kScalesMfma) return launch_pipe<kScalesMfma>(p, out_dtype, stream);
+        if (sf == kScalesRows) return launch_pipe<kScalesRows>(p, out_dtype, stream);
+        return launch_pipe<kScalesBlocks>(p, out_dtype, stream);
     }
     p.tiles_m = uint32_t(M / kTile);
     p.tiles_n = uint32_t(N / kTile);

@@ -156,6 +156,57 @@ def test_contraction_groups_parity(out_dtype):
     assert torch.all(C[1] == 0)
 
 
+@pytest.mark.parametrize("case", ["scale_pitch_not_4", "c_pitch_not_16B", "row_groups_rows_form", "mixed_forms"])
+def test_plain_scale_routes(case):
+    """Plain scales reach the pipelined kernel when both operands' scales are
+    in the rows form (block stride 1, row stride a multiple of 4) or both in
+    the blocks form (row stride 1, block stride a multiple of 4) and C rows
+    are 16-byte pieces; other views take the general kernel.  Each route
+    matches the oracle."""
+    require_gpu()
+    say(f"mx_gemm plain-scale route: {case}")
+    g = np.random.default_rng(31 + len(case))
+    M, N, K = 384, 256, 640
+    A, B = _codes(g, (M, K)), _codes(g, (N, K))
+    if case == "row_groups_rows_form":
+        E = 3
+        Bs = np.stack([_codes(g, (N, K)) for _ in range(E)])
+        sA = g.integers(118, 137, (M, K // 32), dtype=np.uint8)
+        sB = g.integers(118, 137, (E, N, K // 32), dtype=np.uint8)
+        offs = np.array([128, 128, 256], np.int32)
+        C = mxq.mx_grouped_gemm_rows(_dev(A), _dev(sA), _dev(Bs), _dev(sB), _dev(offs))
+        torch.cuda.synchronize()
+        ref, absC = oracle.mx_grouped_gemm_rows(A, sA, Bs, sB, offs, sa_strides=(K // 32, 1),
+                                                sb_strides=(K // 32, 1), threads=THREADS, with_abs=True)
+        _assert_close(C, ref, absC, K, torch.float32, case)
+        assert torch.all(C[offs[-1]:] == 0)
+        return
+    if case == "scale_pitch_not_4":
+        sAw = g.integers(118, 137, (M, K // 32 + 1), dtype=np.uint8)     # row stride 21
+        sBw = g.integers(118, 137, (N, K // 32 + 1), dtype=np.uint8)
+        C = mxq.mx_gemm_nt(_dev(A), _dev(sAw)[:, :K // 32], _dev(B), _dev(sBw)[:, :K // 32])
+        sA, sB = sAw, sBw                                               # read through row stride 21
+        sa, sb = (K // 32 + 1, 1), (K // 32 + 1, 1)
+    elif case == "c_pitch_not_16B":
+        sA = g.integers(118, 137, (M, K // 32), dtype=np.uint8)
+        sB = g.integers(118, 137, (N, K // 32), dtype=np.uint8)
+        out = torch.full((M, N + 1), 5.0, dtype=torch.float32, device=DEV)
+        mxq.mx_gemm_nt(_dev(A), _dev(sA), _dev(B), _dev(sB), out=out[:, :N])
+        C = out[:, :N]
+        sa, sb = (K // 32, 1), (K // 32, 1)
+    else:                                                                 # A rows form, B blocks form
+        sA = g.integers(118, 137, (M, K // 32), dtype=np.uint8)
+        sBc = g.integers(118, 137, (K // 32, N), dtype=np.uint8)
+        C = mxq.mx_gemm_nt(_dev(A), _dev(sA), _dev(B), _dev(sBc).t())
+        sB = sBc
+        sa, sb = (K // 32, 1), (1, N)
+    torch.cuda.synchronize()
+    ref, absC = oracle.mx_gemm_nt(A, sA, B, sB, sa_strides=sa, sb_strides=sb, threads=THREADS, with_abs=True)
+    _assert_close(C, ref, absC, K, torch.float32, case)
+    if case == "c_pitch_not_16B":
+        assert torch.all(out[:, N] == 5.0)
+
+
 def test_consumes_the_cast_outputs_forward_and_weight_gradient():
     """End to end on the device: the dual-axis cast quantizes bf16 operands
     and the contraction consumes its outputs as they are laid out (q_row with

@@ -286,6 +286,13 @@ int mx9_unpack_records(const uint8_t *packed, int64_t ld_p, int64_t outer, int64
  *          cores with fp32 accumulation (summation order unspecified).
  *   M, N, K multiples of 128 (at most 2^24); lda, ldb multiples of 16.
  *
+ * Any scale strides are accepted.  The fast (pipelined) kernel runs when
+ * both operands' scales have block stride 1 and a row stride that is a
+ * multiple of 4, or both have row stride 1 and a block stride that is a
+ * multiple of 4 (the cast's s_row and s_col as above), the scale pointers
+ * are 4-byte aligned and C rows are whole 16-byte pieces; other views take
+ * a slower general kernel with the same results.
+ *
  * Errors: MX_E_NULL, MX_E_DTYPE (out_dtype), MX_E_SHAPE, MX_E_STRIDE (a pitch
  * below its row or misaligned, a negative scale stride), MX_E_ALIGN (A or B
  * not 16-byte aligned, C not aligned to its element), MX_E_OVERLAP (C

@@ -230,7 +230,7 @@ void mx9_unpack_strided(const int8_t* __restrict__ q, const uint8_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // Axis tiles: 64 * kPer inner positions x 32 / kPer blocks of one o per
-// workgroup.  A lane takes kPer adjacent inner positions (kPer = 2 when the
+// workgroup (8 / kPer blocks for the three-part unpack).  A lane takes kPer adjacent inner positions (kPer = 2 when the
 // inner extent is even: one 32-bit load carries two bf16 elements, one 64-bit
 // load two fp32 elements).  The element reads of the pack and the element
 // writes of the unpack (each touched once, in segments scattered over many
@@ -239,10 +239,10 @@ void mx9_unpack_strided(const int8_t* __restrict__ q, const uint8_t* __restrict_
 // 0.47 to 0.71.  Streaming the other side as well is slower.
 // ---------------------------------------------------------------------------
 
-template <int kPer>
+template <int kPer, int kTJ = 32>
 struct Tile {
     static constexpr int kI = 64 * kPer;                 // inner positions per tile
-    static constexpr int kJ = 32 / kPer;                 // blocks per tile row
+    static constexpr int kJ = kTJ / kPer;                // blocks per tile row
     static constexpr int kJW = kJ / 4;                   // blocks per wave
     static constexpr int kQPitch = kJ * 16 + 16;         // q row in LDS (bytes)
     static constexpr int kEPitch = kJ + 4;               // max_exp / prime row in LDS
@@ -250,6 +250,15 @@ struct Tile {
     static constexpr int kQBytes = kI * kQPitch;
     static constexpr int kLds = kI * kRPitch > kI * (kQPitch + 2 * kEPitch) ? kI * kRPitch : kI * (kQPitch + 2 * kEPitch);
 };
+
+// The unpack of the three-part form takes tiles of 8 / kPer blocks per row:
+// their LDS stage is a quarter of the pack's, so four times as many
+// workgroups fit a CU, and measured on MI355X for [4096, 14336] along axis 0
+// the unpack goes from 0.70-0.73 to 0.77-0.82 of peak (the pack is slower
+// with small tiles and keeps 32 / kPer).  Records keep 32 / kPer blocks, so
+// that every row's run of records starts 16-byte aligned.
+template <bool kRecords>
+constexpr int kUnpackTJ = kRecords ? 32 : 8;
 
 struct AxisTiles {
     uint64_t outer, inner;
@@ -264,9 +273,9 @@ struct TileCoord {
     uint32_t j0, rows, nj;    // rows: live inner positions, nj: live blocks per row
 };
 
-template <int kPer>
+template <int kPer, int kTJ = 32>
 __device__ __forceinline__ TileCoord tile_coord(const AxisTiles& v) {
-    using T = Tile<kPer>;
+    using T = Tile<kPer, kTJ>;
     TileCoord c;
     // consecutive workgroups take consecutive inner ranges of the same
     // element rows, so the rows' segments are read (and written) together
@@ -488,12 +497,12 @@ __global__ __launch_bounds__(kThreads)
 void mx9_unpack_axis_tile(const int8_t* __restrict__ q, const uint8_t* __restrict__ max_exp,
                           const uint8_t* __restrict__ prime, const uint8_t* __restrict__ packed, int64_t ld_p,
                           AxisTiles v, void* __restrict__ yv, bool vec_in) {
-    using T = Tile<kPer>;
+    using T = Tile<kPer, kUnpackTJ<kRecords>>;
     __shared__ uint4 lds[T::kLds / 16];
     uint8_t* ls = reinterpret_cast<uint8_t*>(lds);
     uint8_t* ls_e = ls + T::kQBytes;
     uint8_t* ls_p = ls_e + T::kI * T::kEPitch;
-    const TileCoord c = tile_coord<kPer>(v);
+    const TileCoord c = tile_coord<kPer, kUnpackTJ<kRecords>>(v);
     const uint64_t row0 = c.o * v.inner + c.i0;
     if (kRecords) {
         const uint32_t rb = kRec * c.nj;
@@ -564,13 +573,13 @@ void mx9_unpack_axis_tile(const int8_t* __restrict__ q, const uint8_t* __restric
     }
 }
 
-AxisTiles make_tiles(int64_t outer, int64_t len, int64_t inner, int per) {
+AxisTiles make_tiles(int64_t outer, int64_t len, int64_t inner, int per, int tile_tj) {
     AxisTiles v;
     v.outer = uint64_t(outer);
     v.inner = uint64_t(inner);
     v.len = len;
     v.nbl = uint32_t((len + 15) / 16);
-    const int ti = 64 * per, tj = 32 / per;
+    const int ti = 64 * per, tj = tile_tj / per;
     v.tiles_i = uint32_t((inner + ti - 1) / ti);
     v.tiles_j = (v.nbl + uint32_t(tj) - 1) / uint32_t(tj);
     return v;
@@ -601,7 +610,7 @@ template <bool kRecords>
 void launch_pack_tiles(const void* x, int dtype, int64_t outer, int64_t len, int64_t inner, int8_t* q,
                        uint8_t* max_exp, uint8_t* prime, uint8_t* packed, int64_t ld_p, hipStream_t stream) {
     const int per = per_lane(inner, x, dtype == 0 ? 4 : 2);
-    const AxisTiles v = make_tiles(outer, len, inner, per);
+    const AxisTiles v = make_tiles(outer, len, inner, per, 32);
     const dim3 grid(uint32_t(v.outer * v.tiles_i * v.tiles_j));
     const bool vec = aligned16(packed) && ld_p % 16 == 0;
     if (dtype == 0 && per == 2) hipLaunchKernelGGL((mx9_pack_axis_tile<0, kRecords, 2>), grid, dim3(kThreads), 0, stream, x, v, q, max_exp, prime, packed, ld_p, vec);
@@ -615,7 +624,7 @@ void launch_unpack_tiles(const int8_t* q, const uint8_t* max_exp, const uint8_t*
                          int64_t ld_p, int64_t outer, int64_t len, int64_t inner, int out_dtype, void* y,
                          hipStream_t stream) {
     const int per = per_lane(inner, y, out_dtype == 0 ? 4 : 2);
-    const AxisTiles v = make_tiles(outer, len, inner, per);
+    const AxisTiles v = make_tiles(outer, len, inner, per, kUnpackTJ<kRecords>);
     const dim3 grid(uint32_t(v.outer * v.tiles_i * v.tiles_j));
     const bool vec = aligned16(packed) && ld_p % 16 == 0;
     if (out_dtype == 0 && per == 2) hipLaunchKernelGGL((mx9_unpack_axis_tile<0, kRecords, 2>), grid, dim3(kThreads), 0, stream, q, max_exp, prime, packed, ld_p, v, y, vec);

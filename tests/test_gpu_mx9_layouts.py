@@ -57,6 +57,7 @@ SHAPES = [
     ((2, 3, 33), 2),        # last axis through the axis call
     ((17, 4, 600), 0),      # several workgroups of inner positions
     ((5, 300, 70), 1),      # more than 16 blocks per (o, i): several block groups per row
+    ((5, 300, 71), 1),      # the same with an odd inner extent (one inner position per lane)
     ((1, 16, 1), 1),        # one block
 ]
 

@@ -239,17 +239,22 @@ void mx9_unpack_strided(const int8_t* __restrict__ q, const uint8_t* __restrict_
 // 0.47 to 0.71.  Streaming the other side as well is slower.
 // ---------------------------------------------------------------------------
 
-template <int kPer, int kTJ = 32>
+template <int kPer, int kTJ = 32, int kWaves = 4>
 struct Tile {
     static constexpr int kI = 64 * kPer;                 // inner positions per tile
     static constexpr int kJ = kTJ / kPer;                // blocks per tile row
-    static constexpr int kJW = kJ / 4;                   // blocks per wave
+    static constexpr int kJW = kJ / kWaves;              // blocks per wave
     static constexpr int kQPitch = kJ * 16 + 16;         // q row in LDS (bytes)
     static constexpr int kEPitch = kJ + 4;               // max_exp / prime row in LDS
     static constexpr int kRPitch = kJ * kRec + 16;       // record row in LDS
     static constexpr int kQBytes = kI * kQPitch;
     static constexpr int kLds = kI * kRPitch > kI * (kQPitch + 2 * kEPitch) ? kI * kRPitch : kI * (kQPitch + 2 * kEPitch);
 };
+
+// The axis pack runs 8 waves per tile (kJ / 8 blocks each): measured on
+// MI355X this is 1-5% faster than 4 waves of kJ / 4 blocks, with fewer
+// registers per wave and the same LDS stage.
+constexpr int kPackThreads = 512;
 
 // The unpack of the three-part form takes tiles of 8 / kPer blocks per row:
 // their LDS stage is a quarter of the pack's, so four times as many
@@ -367,11 +372,11 @@ __device__ __forceinline__ void stage_block(uint8_t* ls, uint32_t r, uint32_t jl
 }
 
 template <int kDtype, bool kRecords, int kPer>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(kPackThreads)
 void mx9_pack_axis_tile(const void* __restrict__ xv, AxisTiles v, int8_t* __restrict__ q,
                         uint8_t* __restrict__ max_exp, uint8_t* __restrict__ prime,
                         uint8_t* __restrict__ packed, int64_t ld_p, bool vec_out) {
-    using T = Tile<kPer>;
+    using T = Tile<kPer, 32, kPackThreads / 64>;
     __shared__ uint4 lds[T::kLds / 16];
     uint8_t* ls = reinterpret_cast<uint8_t*>(lds);
     const TileCoord c = tile_coord<kPer>(v);
@@ -387,7 +392,7 @@ void mx9_pack_axis_tile(const void* __restrict__ xv, AxisTiles v, int8_t* __rest
     // Batches of kU blocks: every load of a batch is issued before any of its
     // blocks is computed, so 16 * kU loads per lane are in flight.
     using RawT = typename Raw<kDtype, kPer>::type;
-    constexpr int kU = 4;
+    constexpr int kU = T::kJW < 4 ? T::kJW : 4;
     static_assert(T::kJW % kU == 0, "batches divide the wave's blocks");
 #pragma unroll 1
     for (int b0 = 0; b0 < T::kJW; b0 += kU) {
@@ -447,7 +452,7 @@ void mx9_pack_axis_tile(const void* __restrict__ xv, AxisTiles v, int8_t* __rest
     if (kRecords) {
         const uint32_t rb = kRec * c.nj;            // record bytes per row
         const uint32_t chunks = (rb + 15) / 16;
-        for (uint32_t t = threadIdx.x; t < c.rows * chunks; t += kThreads) {
+        for (uint32_t t = threadIdx.x; t < c.rows * chunks; t += kPackThreads) {
             const uint32_t r = t / chunks, k = t - r * chunks;
             uint8_t* dst = packed + (row0 + r) * uint64_t(ld_p) + uint64_t(kRec) * c.j0 + 16u * k;
             const uint8_t* src = ls + r * T::kRPitch + 16u * k;
@@ -461,7 +466,7 @@ void mx9_pack_axis_tile(const void* __restrict__ xv, AxisTiles v, int8_t* __rest
     } else {
         const uint8_t* ls_e = ls + T::kQBytes;
         const uint8_t* ls_p = ls_e + T::kI * T::kEPitch;
-        for (uint32_t t = threadIdx.x; t < c.rows * c.nj; t += kThreads) {
+        for (uint32_t t = threadIdx.x; t < c.rows * c.nj; t += kPackThreads) {
             const uint32_t r = t / c.nj, k = t - r * c.nj;
             const uint64_t blk = (row0 + r) * v.nbl + c.j0 + k;
             reinterpret_cast<uint4*>(q)[blk] = *reinterpret_cast<const uint4*>(ls + r * T::kQPitch + 16u * k);
@@ -613,10 +618,10 @@ void launch_pack_tiles(const void* x, int dtype, int64_t outer, int64_t len, int
     const AxisTiles v = make_tiles(outer, len, inner, per, 32);
     const dim3 grid(uint32_t(v.outer * v.tiles_i * v.tiles_j));
     const bool vec = aligned16(packed) && ld_p % 16 == 0;
-    if (dtype == 0 && per == 2) hipLaunchKernelGGL((mx9_pack_axis_tile<0, kRecords, 2>), grid, dim3(kThreads), 0, stream, x, v, q, max_exp, prime, packed, ld_p, vec);
-    else if (dtype == 0) hipLaunchKernelGGL((mx9_pack_axis_tile<0, kRecords, 1>), grid, dim3(kThreads), 0, stream, x, v, q, max_exp, prime, packed, ld_p, vec);
-    else if (per == 2) hipLaunchKernelGGL((mx9_pack_axis_tile<1, kRecords, 2>), grid, dim3(kThreads), 0, stream, x, v, q, max_exp, prime, packed, ld_p, vec);
-    else hipLaunchKernelGGL((mx9_pack_axis_tile<1, kRecords, 1>), grid, dim3(kThreads), 0, stream, x, v, q, max_exp, prime, packed, ld_p, vec);
+    if (dtype == 0 && per == 2) hipLaunchKernelGGL((mx9_pack_axis_tile<0, kRecords, 2>), grid, dim3(kPackThreads), 0, stream, x, v, q, max_exp, prime, packed, ld_p, vec);
+    else if (dtype == 0) hipLaunchKernelGGL((mx9_pack_axis_tile<0, kRecords, 1>), grid, dim3(kPackThreads), 0, stream, x, v, q, max_exp, prime, packed, ld_p, vec);
+    else if (per == 2) hipLaunchKernelGGL((mx9_pack_axis_tile<1, kRecords, 2>), grid, dim3(kPackThreads), 0, stream, x, v, q, max_exp, prime, packed, ld_p, vec);
+    else hipLaunchKernelGGL((mx9_pack_axis_tile<1, kRecords, 1>), grid, dim3(kPackThreads), 0, stream, x, v, q, max_exp, prime, packed, ld_p, vec);
 }
 
 template <bool kRecords>

@@ -376,7 +376,9 @@ def mx_gemm_nt(A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB: torch.Ten
     """C = A B^T with MXFP8 operands: A [M, K] and B [N, K] E4M3 codes
     (contraction contiguous), sA [M, K/32] and sB [N, K/32] E8M0 scale views
     (e.g. the cast's s_row, or s_col.t() for q_col operands).  C is float32
-    or bfloat16 [M, N]."""
+    or bfloat16 [M, N].  Both scale views in the s_row form (block stride 1)
+    or both in the s_col.t() form (row stride 1), with C rows in 16-byte
+    pieces, take the pipelined kernel; other views a slower general one."""
     _codes(A, "A")
     _codes(B, "B")
     M, K = A.shape

@@ -230,9 +230,9 @@ void mx9_unpack_strided(const int8_t* __restrict__ q, const uint8_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // Axis tiles: 64 * kPer inner positions x 32 / kPer blocks of one o per
-// workgroup (8 / kPer blocks for the three-part unpack).  A lane takes kPer adjacent inner positions (kPer = 2 when the
-// inner extent is even: one 32-bit load carries two bf16 elements, one 64-bit
-// load two fp32 elements).  The element reads of the pack and the element
+// workgroup (8 / kPer blocks for the three-part unpack).  A lane takes kPer
+// adjacent inner positions (kPer = 2 when the inner extent is even: one
+// 32-bit load carries two bf16 elements, one 64-bit load two fp32 elements).  The element reads of the pack and the element
 // writes of the unpack (each touched once, in segments scattered over many
 // rows) carry the non-temporal hint; measured on MI355X for [4096, 14336]
 // along axis 0, pack goes from 0.49 to 0.59 of peak (fp32) and unpack from
@@ -259,7 +259,7 @@ constexpr int kPackThreads = 512;
 // The unpack of the three-part form takes tiles of 8 / kPer blocks per row:
 // their LDS stage is a quarter of the pack's, so four times as many
 // workgroups fit a CU, and measured on MI355X for [4096, 14336] along axis 0
-// the unpack goes from 0.70-0.73 to 0.77-0.82 of peak (the pack is slower
+// the unpack goes from 0.70-0.73 to 0.76-0.85 of peak (the pack is slower
 // with small tiles and keeps 32 / kPer).  Records keep 32 / kPer blocks, so
 // that every row's run of records starts 16-byte aligned.
 template <bool kRecords>

@@ -13,9 +13,12 @@
 //              two-step DPP quad reduction.  Masking the sign makes the
 //              integer order NaN > Inf > finite, so the special cases need no
 //              per-element test.  The cast runs from registers.
-//   * LDS    : the tile is written once (32 KiB).  The column-pair index of
-//              each dword is XORed with the row's 16-row chunk (bits 3..5), so
-//              the colwise reads below are bank-conflict free.
+//   * LDS    : the tile is written once (32 KiB).  The 16-byte chunk index of
+//              each row is XORed with a function of the row's 16-row chunk c
+//              (2c + c/4, lds_chunk_xor), so that the 32 lanes of each half of
+//              a colwise dword read (8 chunks x 4 column pairs) hit 32
+//              distinct banks: SQ_LDS_BANK_CONFLICT reads 0 (with 2c alone,
+//              a two-way conflict, 31% of the LDS-active cycles).
 //   * colwise: a unit is (column pair, 16-row chunk); each thread takes two.
 //              A packed u16 max over 16 LDS dwords plus one DPP step between
 //              the two chunks of a 32-row block gives both column maxima;
@@ -172,6 +175,15 @@ __device__ void validate_offsets(const int32_t* offs, int32_t G, int64_t M, int3
     if (threadIdx.x == 0) *err = first_bad == INT_MAX ? 0 : offs_code(offs, first_bad, M);
 }
 
+// XOR applied to the 16-byte chunk index of the tile rows of 16-row chunk c
+// (0..7) in LDS: 2c | c/4.  A colwise dword read covers 4 column pairs of 8
+// chunks per half wave; 2c spreads the chunks over bits 3..5 of the dword
+// column and c/4 over bit 2, so the half wave's 32 dwords fall in 32 banks.
+__device__ __forceinline__ uint32_t lds_chunk_xor(uint32_t c) {
+    c &= 7u;
+    return (c << 1) | (c >> 2);
+}
+
 // Byte of the tile's 512-byte staging run for local row r (0..127) and local
 // block j (0..3) in the matrix-core scale layout: run r/64, then lane
 // 16 j + r%16, byte (r%64)/16 of its dword.
@@ -228,7 +240,7 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const uint32_t r = 16u * k + rsub;
-        lds_tile[r * 16u + ((t & 15u) ^ (((r >> 4) & 7u) << 1))] = d[k];
+        lds_tile[r * 16u + ((t & 15u) ^ lds_chunk_xor(r >> 4))] = d[k];
         const uint32_t mx = pk_max_u16(pk_max_u16(d[k].x & 0x7FFF7FFFu, d[k].y & 0x7FFF7FFFu),
                                        pk_max_u16(d[k].z & 0x7FFF7FFFu, d[k].w & 0x7FFF7FFFu));
         uint32_t a = max(mx & 0xFFFFu, mx >> 16);
@@ -271,7 +283,7 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const uint32_t cp = ((lane >> 3) & 7u) + 8u * (wave + 4u * u);
-        const uint32_t* src = lt + (16u * c) * 64u + (cp ^ (c << 3));
+        const uint32_t* src = lt + (16u * c) * 64u + (cp ^ (4u * lds_chunk_xor(c)));
         uint32_t v[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = src[i * 64];

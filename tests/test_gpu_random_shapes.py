@@ -153,3 +153,57 @@ def test_scale_conversions_random_views(case):
     back = mxq.scales_from_mfma(flat, R, kb)
     torch.cuda.synchronize()
     _same(back, S, f"case {case} from_mfma")
+
+
+def _codes(g, shape):
+    c = g.integers(0, 256, shape, dtype=np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x38          # no NaN codes
+    return c
+
+
+@pytest.mark.parametrize("case", list(range(10)))
+def test_contraction_random_shapes_and_scale_views(case):
+    """mx_gemm_nt on random shapes with each operand's scales in a random
+    plain form (rows, blocks, with or without a pitch) and a random output
+    pitch, so that every route (the pipelined kernel's two plain forms and
+    the general kernel) is taken; checked against the oracle within the
+    bound the contraction tests derive (2^-10 + (K + 2) 2^-24) sum |a b|."""
+    require_gpu()
+    g = np.random.default_rng(4000 + case)
+    M, N, K = (128 * int(g.integers(1, 5)) for _ in range(3))
+    A, B = _codes(g, (M, K)), _codes(g, (N, K))
+    kb = K // 32
+
+    def scale_view(rows):
+        S = g.integers(118, 137, (rows, kb), dtype=np.uint8)
+        form = int(g.integers(0, 3))
+        if form == 0:                                       # rows form, pitch a multiple of 4 or not
+            pitch = kb + (4 * int(g.integers(0, 2)) if g.integers(0, 3) else 1)
+            buf = np.zeros((rows, pitch), np.uint8)
+            buf[:, :kb] = S
+            return S, torch.from_numpy(buf).to(DEV)[:, :kb], (pitch, 1)
+        if form == 1:                                       # blocks form (a transposed s_col)
+            pitch = rows + 4 * int(g.integers(0, 2))
+            buf = np.zeros((kb, pitch), np.uint8)
+            buf[:, :rows] = S.T
+            return S, torch.from_numpy(buf).to(DEV)[:, :rows].t(), (1, pitch)
+        return S, torch.from_numpy(np.ascontiguousarray(S)).to(DEV), (kb, 1)
+
+    SA, sa_view, sa_str = scale_view(M)
+    SB, sb_view, sb_str = scale_view(N)
+    out_dtype = (torch.float32, torch.bfloat16)[int(g.integers(0, 2))]
+    cpad = (0, 0, 8, 1)[int(g.integers(0, 4))]
+    say(f"random contraction case {case}: [{M}, {N}, {K}] sa {sa_str} sb {sb_str} C pitch N+{cpad} {out_dtype}")
+    out = torch.full((M, N + cpad), 3.0, dtype=out_dtype, device=DEV)
+    mxq.mx_gemm_nt(torch.from_numpy(A).to(DEV), sa_view, torch.from_numpy(B).to(DEV), sb_view, out=out[:, :N])
+    torch.cuda.synchronize()
+    ref, absC = oracle.mx_gemm_nt(A, SA, B, SB, sa_strides=(kb, 1), sb_strides=(kb, 1), threads=THREADS,
+                                  with_abs=True)
+    got = out[:, :N].float().cpu().numpy().astype(np.float64)
+    tol = (2.0 ** -10 + (K + 2) * 2.0 ** -24) * absC
+    if out_dtype == torch.bfloat16:
+        tol = tol + 2.0 ** -8 * np.abs(ref)
+    bad = np.argwhere(~(np.abs(got - ref) <= tol))
+    assert len(bad) == 0, f"case {case}: {len(bad)} entries beyond the bound, first {bad[0].tolist()}"
+    if cpad:
+        assert torch.all(out[:, N:] == 3.0)

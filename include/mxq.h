@@ -313,7 +313,7 @@ int mx_gemm_nt(const uint8_t *A, int64_t lda, const uint8_t *sA, int64_t sa_rs, 
  * [0, M]); otherwise the rows' expert is unspecified but every access stays
  * inside the operands.  Other arguments and errors as for mx_gemm_nt, plus
  * MX_E_SHAPE for G < 1, MX_E_NULL for offs NULL, MX_E_STRIDE for a negative
- * group stride.
+ * group stride.  The pipelined kernel also needs sb_gs to be a multiple of 4.
  */
 int mx_grouped_gemm_rows(const uint8_t *A, int64_t lda, const uint8_t *sA, int64_t sa_rs, int64_t sa_bs,
                          const uint8_t *B, int64_t ldb, int64_t b_gs, const uint8_t *sB, int64_t sb_rs,

@@ -16,17 +16,19 @@
 // both input types.  The quotient x / 2^(E-6-p) is rounded half-to-even
 // in one fused multiply-add with 1.5 * 2^23 (its reciprocal is a normal
 // float for every block whose exponent byte is at least 9; smaller blocks
-// form it exactly with v_ldexp_f32), and clamped with one median.  A wave
-// issues one 16-byte load per lane: four loads per lane before computing
-// measured no faster in the cast -> pack -> unpack sequence on MI355X.
+// form it exactly with v_ldexp_f32), and clamped with one median.  A lane of
+// the flat pack issues eight 16-byte loads before it quantizes any of them.
 //
 // Cache policy of the flat kernels (each byte is touched once): the pack
-// reads its input and writes q, max_exp and prime with the non-temporal
-// hint, the unpack writes its output with it.  Measured on MI355X, ordinary
-// write-back stores leave the memory-side cache full of dirty lines that the
-// next kernel pays for: in the sequence cast -> pack -> unpack the streaming
+// reads its input and writes q with the non-temporal hint, the unpack writes
+// its output with it.  Measured on MI355X, ordinary write-back stores of the
+// bulk streams leave the memory-side cache full of dirty lines that the next
+// kernel pays for: in the sequence cast -> pack -> unpack the streaming
 // policy brings the step from 5.59 to 5.85 TB/s and the cast after it from
-// 206 to 196 us, and the unpack alone from 0.65-0.68 to 0.84 of peak.
+// 206 to 196 us, and the unpack alone from 0.65-0.68 to 0.84 of peak.  The
+// pack's max_exp and prime bytes (1/16 of its output each) are the
+// exception: ordinary stores, which the cache merges into whole lines, are
+// faster in that sequence than streaming single bytes.
 #include "mxq_kernels.h"
 #include "mx9_codec.h"
 
@@ -112,44 +114,77 @@ void mx9_pack_any(const void* __restrict__ xv, int64_t ld_x, int64_t cols, uint3
 // prime bits are combined across the L lanes with DPP quad permutes.
 // ---------------------------------------------------------------------------
 
-// One pass of the flat pack: this lane's 16-byte piece of block blk.
-template <int kDtype, bool kGuard>
-__device__ __forceinline__ void pack_piece(const void* __restrict__ xv, uint64_t nb, uint64_t blk,
-                                           uint32_t part, int8_t* __restrict__ q,
-                                           uint8_t* __restrict__ max_exp, uint8_t* __restrict__ prime) {
+// Groups of 64 / kLanes blocks (one wave-wide 1 KiB load) that one wave of
+// the flat pack takes; their loads are all issued before the first group is
+// quantized.
+constexpr int kPackGroups = 8;
+
+// Quantize one loaded 16-byte piece (this lane's share of block blk) and store
+// its outputs: q with the non-temporal hint, the max_exp and prime bytes with
+// ordinary write-back stores (the cache merges the wave's 1-byte stores).
+template <int kDtype>
+__device__ __forceinline__ void pack_piece_store(uint4 d, uint64_t blk, uint32_t part, int8_t* __restrict__ q,
+                                                 uint8_t* __restrict__ max_exp, uint8_t* __restrict__ prime) {
     using P = FlatPiece<kDtype>;
-    const bool live = !kGuard || blk < nb;
-    uint4 d = make_uint4(0u, 0u, 0u, 0u);
-    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-    if (live) {
-        const u4 v = __builtin_nontemporal_load(reinterpret_cast<const u4*>(xv) + blk * P::kLanes + part);
-        d = make_uint4(v.x, v.y, v.z, v.w);
-    }
     const P r = pack_flat_piece<kDtype>(d, part);
-    if (live) {
-        uint8_t* qb = reinterpret_cast<uint8_t*>(q) + blk * 16 + part * P::kElems;
-        typedef unsigned int u2 __attribute__((ext_vector_type(2)));
-        if (P::kElems == 8) __builtin_nontemporal_store(u2{r.qd[0], r.qd[1]}, reinterpret_cast<u2*>(qb));
-        else __builtin_nontemporal_store(r.qd[0], reinterpret_cast<uint32_t*>(qb));
-        if (part == 0) __builtin_nontemporal_store(uint8_t(r.S), max_exp + blk);
-        if (part == 1) __builtin_nontemporal_store(uint8_t(r.prime), prime + blk);
-    }
+    uint8_t* qb = reinterpret_cast<uint8_t*>(q) + blk * 16 + part * P::kElems;
+    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+    if (P::kElems == 8) __builtin_nontemporal_store(u2{r.qd[0], r.qd[1]}, reinterpret_cast<u2*>(qb));
+    else __builtin_nontemporal_store(r.qd[0], reinterpret_cast<uint32_t*>(qb));
+    if (part == 0) max_exp[blk] = uint8_t(r.S);
+    if (part == 1) prime[blk] = uint8_t(r.prime);
 }
 
 // kDtype 0: fp32, 4 lanes x 4 elements per block.  1: bf16, 2 lanes x 8.
-// Each wave owns 64 / kLanes consecutive blocks: one contiguous 1 KiB load.
+// Each wave owns kPackGroups groups of 64 / kLanes consecutive blocks; group k
+// is one contiguous 1 KiB load.  A lane issues its kPackGroups streaming loads
+// before it quantizes anything, so a wave keeps 8 KiB of reads in flight.
+// Measured on MI355X (bf16 [32768, 8192], rotating buffers): one group per
+// wave 157 us, two 133 us, eight 127 us; in the cast -> pack -> unpack
+// sequence the step went from 471 us to 452 us.  Streaming the max_exp and
+// prime bytes as well costs 4% (one group) to 7% (two groups) in the step.
 template <int kDtype>
 __global__ __launch_bounds__(kThreads)
 void mx9_pack_flat(const void* __restrict__ xv, uint64_t nb, int8_t* __restrict__ q,
                    uint8_t* __restrict__ max_exp, uint8_t* __restrict__ prime) {
     constexpr int kLanes = kDtype == 0 ? 4 : 2;
+    constexpr uint32_t kGroup = 64 / kLanes;
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t part = lane % kLanes;
-    const uint64_t wave_blk0 = (uint64_t(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6)) * (64 / kLanes);
-    if (wave_blk0 + 64 / kLanes <= nb)
-        pack_piece<kDtype, false>(xv, nb, wave_blk0 + lane / kLanes, part, q, max_exp, prime);
-    else
-        pack_piece<kDtype, true>(xv, nb, wave_blk0 + lane / kLanes, part, q, max_exp, prime);
+    const uint64_t blk0 = (uint64_t(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6)) * (kPackGroups * kGroup);
+    const u4* src = reinterpret_cast<const u4*>(xv) + blk0 * kLanes + lane;
+    if (blk0 + kPackGroups * kGroup <= nb) {
+        u4 v[kPackGroups];
+#pragma unroll
+        for (int k = 0; k < kPackGroups; ++k) v[k] = __builtin_nontemporal_load(src + k * 64);
+#pragma unroll
+        for (int k = 0; k < kPackGroups; ++k)
+            pack_piece_store<kDtype>(make_uint4(v[k].x, v[k].y, v[k].z, v[k].w), blk0 + k * kGroup + lane / kLanes,
+                                     part, q, max_exp, prime);
+    } else {
+        // the last wave: groups past nb are skipped, a partial group is guarded per block
+        for (int k = 0; k < kPackGroups; ++k) {
+            const uint64_t blk = blk0 + k * kGroup + lane / kLanes;
+            if (blk0 + k * kGroup >= nb) break;
+            uint4 d = make_uint4(0u, 0u, 0u, 0u);
+            if (blk < nb) {
+                const u4 v = __builtin_nontemporal_load(src + k * 64);
+                d = make_uint4(v.x, v.y, v.z, v.w);
+            }
+            // every lane of the wave takes part in the DPP combines; only live blocks store
+            using P = FlatPiece<kDtype>;
+            const P r = pack_flat_piece<kDtype>(d, part);
+            if (blk < nb) {
+                uint8_t* qb = reinterpret_cast<uint8_t*>(q) + blk * 16 + part * P::kElems;
+                typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+                if (P::kElems == 8) __builtin_nontemporal_store(u2{r.qd[0], r.qd[1]}, reinterpret_cast<u2*>(qb));
+                else __builtin_nontemporal_store(r.qd[0], reinterpret_cast<uint32_t*>(qb));
+                if (part == 0) max_exp[blk] = uint8_t(r.S);
+                if (part == 1) prime[blk] = uint8_t(r.prime);
+            }
+        }
+    }
 }
 
 // kOut 0: fp32 output, 4 lanes x 4 elements per block.  1: bf16, 2 lanes x 8.
@@ -249,8 +284,9 @@ hipError_t launch_mx9_pack(const void* x, int dtype, int64_t rows, int64_t cols,
     const dim3 grid(uint32_t((nb + kThreads - 1) / kThreads));
     const bool vec = cols % 16 == 0 && aligned16(x) && (ld_x * esz) % 16 == 0;
     if (vec && ld_x == cols && aligned16(q)) {
-        // 64 / kLanes blocks per wave, 4 waves per workgroup
-        const dim3 fgrid(uint32_t((nb + (dtype == 0 ? 63 : 127)) / (dtype == 0 ? 64 : 128)));
+        // kPackGroups * 64 / kLanes blocks per wave, 4 waves per workgroup
+        const uint64_t per_wg = uint64_t(kThreads / 64) * kPackGroups * (dtype == 0 ? 16 : 32);
+        const dim3 fgrid(uint32_t((nb + per_wg - 1) / per_wg));
         if (dtype == 0) hipLaunchKernelGGL(mx9_pack_flat<0>, fgrid, dim3(kThreads), 0, stream, x, nb, q, max_exp, prime);
         else hipLaunchKernelGGL(mx9_pack_flat<1>, fgrid, dim3(kThreads), 0, stream, x, nb, q, max_exp, prime);
         return hipGetLastError();

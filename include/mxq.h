@@ -177,7 +177,8 @@ int mx_quantize_grouped_mfma(const uint16_t *x, int64_t M, int64_t N, int64_t ld
  *
  * Errors: MX_E_NULL, MX_E_DTYPE (dtype not F32/BF16), MX_E_BLOCK
  * (block_size != 16), MX_E_SHAPE (negative or too large), MX_E_STRIDE
- * (ld_x < cols), MX_E_ALIGN (x not aligned to its element size, q not
+ * (ld_x < cols, or x spanning more than 2^48 bytes), MX_E_ALIGN (x not
+ * aligned to its element size, q not
  * 16-byte aligned), MX_E_OVERLAP.  rows == 0 or cols == 0 is a no-op.
  */
 int mx9_pack(const void *x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld_x,
@@ -197,7 +198,8 @@ int mx9_pack(const void *x, int32_t dtype, int64_t rows, int64_t cols, int64_t l
  *   columns of each row are written.
  *
  * Errors: MX_E_NULL, MX_E_DTYPE, MX_E_BLOCK, MX_E_SHAPE, MX_E_STRIDE
- * (ld_y < cols), MX_E_ALIGN (q not 16-byte aligned, y not aligned to its
+ * (ld_y < cols, or y spanning more than 2^48 bytes), MX_E_ALIGN (q not
+ * 16-byte aligned, y not aligned to its
  * element size), MX_E_OVERLAP.  rows == 0 or cols == 0 is a no-op.
  */
 int mx9_unpack(const int8_t *q, const uint8_t *max_exp, const uint8_t *prime,
@@ -252,7 +254,8 @@ int mx9_unpack_axis(const int8_t *q, const uint8_t *max_exp, const uint8_t *prim
  *           written.  9 bits per element.
  *
  * Errors: MX_E_NULL, MX_E_DTYPE, MX_E_BLOCK, MX_E_SHAPE, MX_E_STRIDE
- * (ld_p < 18 * nbl or above 2^40), MX_E_ALIGN (x not aligned to its element
+ * (ld_p < 18 * nbl or above 2^40, or the records spanning more than 2^48
+ * bytes), MX_E_ALIGN (x not aligned to its element
  * size), MX_E_OVERLAP.  A zero dimension is a no-op.  Contiguous records of
  * a last-axis pack whose len is a multiple of 16, with x and packed 16-byte
  * aligned, take the fastest path.
@@ -264,7 +267,8 @@ int mx9_pack_records(const void *x, int32_t dtype, int64_t outer, int64_t len, i
  * mx9_unpack_records -- inverse of mx9_pack_records into a contiguous
  * [outer, len, inner] y of out_dtype (fp32 or bf16), computed as in
  * mx9_unpack.  Errors: MX_E_NULL, MX_E_DTYPE, MX_E_BLOCK, MX_E_SHAPE,
- * MX_E_STRIDE, MX_E_ALIGN (y not aligned to its element size), MX_E_OVERLAP.
+ * MX_E_STRIDE (as for mx9_pack_records), MX_E_ALIGN (y not aligned to its
+ * element size), MX_E_OVERLAP.
  */
 int mx9_unpack_records(const uint8_t *packed, int64_t ld_p, int64_t outer, int64_t len, int64_t inner,
                        int32_t block_size, int32_t out_dtype, void *y, void *stream);

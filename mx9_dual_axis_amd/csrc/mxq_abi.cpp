@@ -38,10 +38,17 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 uintptr_t addr(const void* p) { return reinterpret_cast<uintptr_t>(p); }
 
-// Bytes spanned by a [rows, cols] matrix with row pitch ld (elements).
+// No device buffer spans more bytes than a 48-bit virtual address space.
+constexpr uint64_t kMaxSpan = uint64_t(1) << 48;
+constexpr uint64_t kTooLarge = ~uint64_t(0);
+
+// Bytes spanned by a [rows, cols] matrix with row pitch ld (elements), or
+// kTooLarge when that exceeds kMaxSpan (computed without overflow).
 uint64_t matrix_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t esz) {
     if (rows <= 0 || cols <= 0) return 0;
-    return uint64_t((rows - 1) * ld + cols) * uint64_t(esz);
+    const unsigned __int128 b =
+        (static_cast<unsigned __int128>(rows - 1) * uint64_t(ld) + uint64_t(cols)) * uint64_t(esz);
+    return b > kMaxSpan ? kTooLarge : uint64_t(b);
 }
 
 int check_dual(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x, int32_t block_size,
@@ -297,8 +304,10 @@ int mx9_pack(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t l
     if (nb > kMaxThreads) return MX_E_SHAPE;
     if (ld_x < cols || ld_x > (int64_t(1) << 40)) return MX_E_STRIDE;
     const int64_t esz = dtype == MX_DTYPE_F32 ? 4 : 2;
+    const uint64_t xb = matrix_bytes(rows, cols, ld_x, esz);
+    if (xb == kTooLarge) return MX_E_STRIDE;
     if (!empty && (!aligned(x, uintptr_t(esz)) || !aligned(q, 16))) return MX_E_ALIGN;
-    const Span s[4] = {{addr(x), matrix_bytes(rows, cols, ld_x, esz)}, {addr(q), nb * 16},
+    const Span s[4] = {{addr(x), xb}, {addr(q), nb * 16},
                        {addr(max_exp), nb}, {addr(prime), nb}};
     if (any_overlap(s, 4)) return MX_E_OVERLAP;
     if (nb == 0) return MX_OK;
@@ -319,9 +328,10 @@ int mx9_unpack(const int8_t* q, const uint8_t* max_exp, const uint8_t* prime,
     if (nb > kMaxThreads) return MX_E_SHAPE;
     if (ld_y < cols || ld_y > (int64_t(1) << 40)) return MX_E_STRIDE;
     const int64_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
+    const uint64_t yb = matrix_bytes(rows, cols, ld_y, esz);
+    if (yb == kTooLarge) return MX_E_STRIDE;
     if (!empty && (!aligned(q, 16) || !aligned(y, uintptr_t(esz)))) return MX_E_ALIGN;
-    const Span s[4] = {{addr(q), nb * 16}, {addr(max_exp), nb}, {addr(prime), nb},
-                       {addr(y), matrix_bytes(rows, cols, ld_y, esz)}};
+    const Span s[4] = {{addr(q), nb * 16}, {addr(max_exp), nb}, {addr(prime), nb}, {addr(y), yb}};
     if (any_overlap(s, 4)) return MX_E_OVERLAP;
     if (nb == 0) return MX_OK;
     hipError_t e = mxq::launch_mx9_unpack(q, max_exp, prime, rows, cols, out_dtype, y, ld_y,
@@ -376,10 +386,11 @@ int mx9_pack_records(const void* x, int32_t dtype, int64_t outer, int64_t len, i
     if (rc != MX_OK) return rc;
     const int64_t row_bytes = 18 * ((len + 15) / 16);
     if (ld_p < row_bytes || ld_p > (int64_t(1) << 40)) return MX_E_STRIDE;
+    const uint64_t pb = matrix_bytes(outer * inner, row_bytes, ld_p, 1);
+    if (pb == kTooLarge) return MX_E_STRIDE;
     const uint64_t esz = dtype == MX_DTYPE_F32 ? 4 : 2;
     if (!empty && !aligned(x, uintptr_t(esz))) return MX_E_ALIGN;
-    const Span s[2] = {{addr(x), uint64_t(outer) * uint64_t(len) * uint64_t(inner) * esz},
-                       {addr(packed), matrix_bytes(outer * inner, row_bytes, ld_p, 1)}};
+    const Span s[2] = {{addr(x), uint64_t(outer) * uint64_t(len) * uint64_t(inner) * esz}, {addr(packed), pb}};
     if (any_overlap(s, 2)) return MX_E_OVERLAP;
     if (nb == 0) return MX_OK;
     hipError_t e = mxq::launch_mx9_pack_records(x, dtype, outer, len, inner, packed, ld_p,
@@ -396,10 +407,11 @@ int mx9_unpack_records(const uint8_t* packed, int64_t ld_p, int64_t outer, int64
     if (rc != MX_OK) return rc;
     const int64_t row_bytes = 18 * ((len + 15) / 16);
     if (ld_p < row_bytes || ld_p > (int64_t(1) << 40)) return MX_E_STRIDE;
+    const uint64_t pb = matrix_bytes(outer * inner, row_bytes, ld_p, 1);
+    if (pb == kTooLarge) return MX_E_STRIDE;
     const uint64_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
     if (!empty && !aligned(y, uintptr_t(esz))) return MX_E_ALIGN;
-    const Span s[2] = {{addr(packed), matrix_bytes(outer * inner, row_bytes, ld_p, 1)},
-                       {addr(y), uint64_t(outer) * uint64_t(len) * uint64_t(inner) * esz}};
+    const Span s[2] = {{addr(packed), pb}, {addr(y), uint64_t(outer) * uint64_t(len) * uint64_t(inner) * esz}};
     if (any_overlap(s, 2)) return MX_E_OVERLAP;
     if (nb == 0) return MX_OK;
     hipError_t e = mxq::launch_mx9_unpack_records(packed, ld_p, outer, len, inner, out_dtype, y,

@@ -102,6 +102,10 @@ def test_mx9_validation_codes():
     assert unpack(ld=10) == 6 and unpack(y=FAKE * 5 + 2) == 7 and unpack(q=FAKE * 2 + 8) == 7
     assert unpack(y=FAKE * 2 + 64) == 8
     assert unpack(cols=0, y=None, q=None, e=None, p=None) == 0
+    # a pitch that makes the matrix span more than any address space is rejected
+    # before anything else is computed from it (no 64-bit overflow)
+    assert pack(rows=1 << 31, cols=1, ld=1 << 40) == 6 and unpack(rows=1 << 31, cols=1, ld=1 << 40) == 6
+    assert pack(rows=1 << 20, cols=16, ld=1 << 29) == 6 and pack(rows=1 << 10, cols=16, ld=1 << 29, x=FAKE) == 8
 
 
 def test_mx9_axis_and_record_validation_codes():
@@ -133,6 +137,8 @@ def test_mx9_axis_and_record_validation_codes():
     assert pack_rec(x=FAKE + 2) == 7
     assert pack_rec(pk=FAKE + 64) == 8                            # records inside the input
     assert pack_rec(length=0, x=None, pk=None) == 0
+    assert pack_rec(outer=1 << 20, inner=1 << 11, length=16, ld=1 << 40) == 6
+    assert unpack_rec(outer=1 << 20, inner=1 << 11, length=16, ld=1 << 40) == 6
     assert unpack_rec(pk=None) == 1 and unpack_rec(od=2) == 2 and unpack_rec(ld=10) == 6
     assert unpack_rec(y=FAKE * 5 + 2) == 7 and unpack_rec(y=FAKE * 2 + 100) == 8
     assert unpack_rec(inner=0, y=None, pk=None) == 0

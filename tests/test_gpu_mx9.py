@@ -56,7 +56,8 @@ def _check_unpack(q, e, p, rows, cols, tag, out_dtype="fp32"):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-@pytest.mark.parametrize("rows,cols", [(16, 64), (64, 1024), (33, 200), (7, 5), (128, 4096), (1, 16)])
+@pytest.mark.parametrize("rows,cols", [(16, 64), (64, 1024), (33, 200), (7, 5), (128, 4096), (1, 16),
+                                       (5, 128), (3, 4112), (9, 2048)])
 def test_pack_unpack_parity(dtype, rows, cols):
     require_gpu()
     say(f"mx9 parity {dtype} [{rows}, {cols}]")

@@ -82,7 +82,7 @@ def test_axis_pack_unpack_parity(shape, axis, kind):
 
 
 @pytest.mark.parametrize("kind", ["fp32", "bf16"])
-@pytest.mark.parametrize("shape,axis", SHAPES + [((96, 256), 1), ((1000, 64), 1), ((7, 4096), 1)])
+@pytest.mark.parametrize("shape,axis", SHAPES + [((96, 256), 1), ((1000, 64), 1), ((7, 4096), 1), ((3, 4112), 1)])
 def test_records_pack_unpack_parity(shape, axis, kind):
     """Records of the same blocks: the flat path (last axis, length a multiple
     of 16, contiguous records) and the strided path (everything else)."""

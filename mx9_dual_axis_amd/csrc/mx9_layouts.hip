@@ -17,11 +17,11 @@
 //   * flat records: contiguous input blocks and contiguous records.  The
 //     lanes hold blocks exactly as the flat three-part pack does (a block
 //     over 2 lanes for bf16, 4 for fp32; every wave-wide load is one
-//     contiguous range).  A workgroup of the pack takes eight groups of 128
-//     (bf16) or 64 (fp32) blocks and issues all their loads first; its
-//     records are assembled in LDS and written as 16-byte chunks, so the
-//     18-byte records cost no unaligned global stores.  The unpack stages
-//     the records the same way.
+//     contiguous range).  A wave of the pack takes four groups of 32 (bf16)
+//     or 16 (fp32) contiguous blocks and issues all their loads first; its
+//     records are assembled in the wave's own slice of LDS and written as
+//     16-byte chunks, so the 18-byte records cost no unaligned global
+//     stores.  The unpack stages a workgroup's records the same way.
 //   * axis tiles (inner > 1): a workgroup takes 64 consecutive inner
 //     positions i of one o and 32 consecutive blocks j (128 and 16 when the
 //     inner extent is even: a lane then takes two adjacent i, so one 32-bit
@@ -57,46 +57,53 @@ __device__ __forceinline__ uint32_t load_bits(const void* xv, uint64_t idx, int 
 // Flat records
 // ---------------------------------------------------------------------------
 
-// Groups of kThreads / kLanes blocks that one workgroup of the flat record
-// pack takes; a lane issues the (streaming) loads of all its groups before it
-// quantizes any of them.  With one group per workgroup the pack ran at
-// 0.64-0.66 of peak on the [4096, 14336] weights.
-constexpr int kRecGroups = 8;
+// Groups of 64 / kLanes blocks (one wave-wide 1 KiB load) that one wave of
+// the flat record pack takes.  A wave's blocks are contiguous, so are its
+// records, and it stages them in its own slice of LDS: no workgroup barrier.
+// Measured on MI355X for the [4096, 14336] weights (byte-identical output):
+// one workgroup-wide stage of 8 x 256 lanes' blocks 58-60 us (fp32) and
+// 32.5-32.8 us (bf16); per-wave stages of 4 groups 54.4 us and 30.1 us.
+constexpr int kRecGroups = 4;
 
 template <int kDtype>
 __global__ __launch_bounds__(kThreads)
 void mx9_pack_records_flat(const void* __restrict__ xv, uint64_t nb, uint8_t* __restrict__ packed) {
     using P = FlatPiece<kDtype>;
-    constexpr int kBlocks = kThreads / P::kLanes;                 // 128 (bf16) or 64 (fp32) per group
-    __shared__ uint4 stage[kRecGroups * kBlocks * kRec / 16];      // 18 KiB or 9 KiB
+    constexpr int kGB = 64 / P::kLanes;                          // blocks per group (16 or 32)
+    constexpr int kWB = kRecGroups * kGB;                        // blocks per wave (64 or 128)
+    constexpr int kBytes = kWB * kRec;                           // record bytes per wave (1152 or 2304)
+    static_assert(kBytes % 16 == 0, "a wave's records are whole 16-byte chunks");
+    __shared__ uint4 stage[kThreads / 64][kBytes / 16];
     typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-    uint8_t* st = reinterpret_cast<uint8_t*>(stage);
-    const uint64_t blk0 = uint64_t(blockIdx.x) * (kRecGroups * kBlocks);
-    const uint32_t lb = threadIdx.x / P::kLanes, part = threadIdx.x % P::kLanes;
-    const u4* src = reinterpret_cast<const u4*>(xv) + blk0 * P::kLanes + threadIdx.x;
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    uint8_t* st = reinterpret_cast<uint8_t*>(stage[wave]);
+    const uint64_t blk0 = (uint64_t(blockIdx.x) * (kThreads / 64) + wave) * kWB;
+    if (blk0 >= nb) return;                                      // uniform across the wave
+    const uint32_t part = lane % P::kLanes, lb = lane / P::kLanes;
+    const u4* src = reinterpret_cast<const u4*>(xv) + blk0 * P::kLanes + lane;
     u4 v[kRecGroups];
 #pragma unroll
     for (int k = 0; k < kRecGroups; ++k) {
         v[k] = u4{0u, 0u, 0u, 0u};
-        if (blk0 + k * kBlocks + lb < nb) v[k] = __builtin_nontemporal_load(src + k * kThreads);
+        if (blk0 + k * kGB + lb < nb) v[k] = __builtin_nontemporal_load(src + k * 64);
     }
 #pragma unroll
     for (int k = 0; k < kRecGroups; ++k) {
         const P r = pack_flat_piece<kDtype>(make_uint4(v[k].x, v[k].y, v[k].z, v[k].w), part);
-        uint8_t* rec = st + kRec * (k * kBlocks + lb);
+        uint8_t* rec = st + kRec * (k * kGB + lb);
         if (part == 0) rec[0] = uint8_t(r.S);
         if (part == P::kLanes - 1) rec[kRec - 1] = uint8_t(r.prime);
 #pragma unroll
         for (int e = 0; e < P::kElems; ++e) rec[1 + part * P::kElems + e] = uint8_t(r.qd[e >> 2] >> (8 * (e & 3)));
     }
-    __syncthreads();
-    // the workgroup's records are one contiguous, 16-byte aligned range
-    const uint64_t live = nb - blk0 < uint64_t(kRecGroups * kBlocks) ? nb - blk0 : uint64_t(kRecGroups * kBlocks);
-    const uint32_t nbytes = uint32_t(live) * kRec;
+    __builtin_amdgcn_s_waitcnt(0xC07F);                         // lgkmcnt(0): the wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    // the wave's records are one contiguous, 16-byte aligned range
+    const uint32_t nbytes = uint32_t(nb - blk0 < uint64_t(kWB) ? nb - blk0 : uint64_t(kWB)) * kRec;
     uint8_t* out = packed + blk0 * kRec;
-    for (uint32_t c = threadIdx.x; c * 16u < nbytes; c += kThreads) {
+    for (uint32_t c = lane; c * 16u < nbytes; c += 64u) {
         if (c * 16u + 16u <= nbytes) {
-            const uint4 w = stage[c];
+            const uint4 w = stage[wave][c];
             __builtin_nontemporal_store(u4{w.x, w.y, w.z, w.w}, reinterpret_cast<u4*>(out) + c);
         } else {
             for (uint32_t b = c * 16u; b < nbytes; ++b) out[b] = st[b];
@@ -693,7 +700,7 @@ hipError_t launch_mx9_pack_records(const void* x, int dtype, int64_t outer, int6
     const int64_t nbl = (len + 15) / 16;
     if (inner == 1 && len % 16 == 0 && ld_p == kRec * nbl && aligned16(x) && aligned16(packed)) {
         const uint64_t nb = uint64_t(outer) * uint64_t(nbl);
-        const uint64_t per_wg = uint64_t(kRecGroups) * (dtype == 0 ? 64u : 128u);
+        const uint64_t per_wg = uint64_t(kThreads / 64) * kRecGroups * (dtype == 0 ? 16u : 32u);
         const dim3 grid(uint32_t((nb + per_wg - 1) / per_wg));
         if (dtype == 0) hipLaunchKernelGGL(mx9_pack_records_flat<0>, grid, dim3(kThreads), 0, stream, x, nb, packed);
         else hipLaunchKernelGGL(mx9_pack_records_flat<1>, grid, dim3(kThreads), 0, stream, x, nb, packed);

@@ -26,7 +26,9 @@ the mixed-magnitude bf16 [8192, 7168] matrix, the grouped cast of bf16
 one tensor of 18-byte records, and three tensors along axis 0; the casts and
 contractions in the matrix-core scale layout; and the dual-axis cast of the
 stress matrix timed alone (back-to-back calls), to compare with its time
-inside the step.
+inside the step.  Each workload is also timed back to back between one pair
+of events over the same rotation (``back_to_back_us``), which leaves out the
+idle time of the per-call event records.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--skip-cpu] [--skip-configs]
 """
@@ -150,9 +152,17 @@ class HipEvent:
             self._hip.hipEventDestroy(self.h)
 
 
+class Timings(list):
+    """Per-call durations in seconds; `back_to_back` is the average duration
+    of the same calls launched back to back between one pair of events."""
+    back_to_back = None
+
+
 def time_rotating(calls, launches: int):
     """Per-call durations (seconds, from HIP events on the launch stream) of
-    `launches` calls cycling through `calls` (one per buffer set)."""
+    `launches` calls cycling through `calls` (one per buffer set).  Each
+    bracketed call also holds the idle time of its two event records (about
+    5 us on MI355X), so the same calls are then timed back to back as well."""
     import torch
     for c in calls:
         c()
@@ -166,15 +176,28 @@ def time_rotating(calls, launches: int):
         calls[i % len(calls)]()
         b.record()
     torch.cuda.synchronize()
-    return [a.elapsed_time(b) * 1e-3 for a, b in evs]
+    ts = Timings(a.elapsed_time(b) * 1e-3 for a, b in evs)
+    e0, e1 = HipEvent(), HipEvent()
+    e0.record()
+    for i in range(launches):
+        calls[i % len(calls)]()
+    e1.record()
+    torch.cuda.synchronize()
+    ts.back_to_back = e0.elapsed_time(e1) * 1e-3 / launches
+    return ts
 
 
 def summarize(ts, nbytes):
+    b2b = getattr(ts, "back_to_back", None)
     ts = sorted(ts)
     med = ts[len(ts) // 2]
     mean = sum(ts) / len(ts)
-    return {"us": round(mean * 1e6, 2), "median_us": round(med * 1e6, 2), "bytes": int(nbytes),
-            "GB_s": round(nbytes / mean / 1e9, 1), "frac": round(nbytes / mean / 1e9 / PEAK_HBM_GBS, 4)}
+    out = {"us": round(mean * 1e6, 2), "median_us": round(med * 1e6, 2), "bytes": int(nbytes),
+           "GB_s": round(nbytes / mean / 1e9, 1), "frac": round(nbytes / mean / 1e9 / PEAK_HBM_GBS, 4)}
+    if b2b:
+        out.update({"back_to_back_us": round(b2b * 1e6, 2), "back_to_back_GB_s": round(nbytes / b2b / 1e9, 1),
+                    "back_to_back_frac": round(nbytes / b2b / 1e9 / PEAK_HBM_GBS, 4)})
+    return out
 
 
 def measure_configs(dev, launches: int, sets: int = 3):
@@ -297,15 +320,19 @@ def measure_gemm(dev, launches: int):
         """Rates against both roofs; `bound` is the one that limits the
         workload at peak (time at the roof = the larger of FLOP / 5.0 PFLOP/s
         and minimal HBM bytes / 8 TB/s), `frac` = that time / measured time."""
+        b2b = getattr(ts, "back_to_back", None)
         ts = sorted(ts)
         mean = sum(ts) / len(ts)
         tf = flops / mean / 1e12
         t_mfma = flops / (PEAK_FP8_TFLOPS * 1e12)
         t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
-        return {"workload": workload, "us": round(mean * 1e6, 2), "median_us": round(ts[len(ts) // 2] * 1e6, 2),
-                "flop": int(flops), "hbm_bytes": int(nbytes), "TFLOP_s": round(tf, 1),
-                "GB_s": round(nbytes / mean / 1e9, 1), "bound": "mfma" if t_mfma >= t_hbm else "hbm",
-                "frac": round(max(t_mfma, t_hbm) / mean, 4)}
+        out = {"workload": workload, "us": round(mean * 1e6, 2), "median_us": round(ts[len(ts) // 2] * 1e6, 2),
+               "flop": int(flops), "hbm_bytes": int(nbytes), "TFLOP_s": round(tf, 1),
+               "GB_s": round(nbytes / mean / 1e9, 1), "bound": "mfma" if t_mfma >= t_hbm else "hbm",
+               "frac": round(max(t_mfma, t_hbm) / mean, 4)}
+        if b2b:
+            out.update({"back_to_back_us": round(b2b * 1e6, 2), "back_to_back_frac": round(max(t_mfma, t_hbm) / b2b, 4)})
+        return out
 
     print("bench: MXFP8 contractions (grouped forward, weight gradient, dense)", file=sys.stderr, flush=True)
     g = np.random.default_rng(11)

@@ -505,7 +505,19 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     copy_gbs = 2 * half * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
+    # and the same volume through torch's vectorized elementwise kernel (a
+    # streaming read and write of 16-byte pieces; hipMemcpyAsync's copy kernel
+    # is slower on MI355X)
+    src32, dst32 = src.view(torch.int32), dst.view(torch.int32)
+    torch.bitwise_not(src32, out=dst32)
+    e0, e1 = HipEvent(), HipEvent()
+    e0.record()
+    for _ in range(10):
+        torch.bitwise_not(src32, out=dst32)
+    e1.record()
+    torch.cuda.synchronize()
+    stream_gbs = 2 * half * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst, src32, dst32
 
     # context: the dual-axis cast alone on the same matrix, back-to-back calls
     # alternating two output sets (the 1.09 GB per call exceeds the 256 MB
@@ -545,6 +557,7 @@ def main():
                      "timed_every_nth_step": EVENT_EVERY},
         "kernels": kernels,
         "copy_GB_s": round(copy_gbs, 1),
+        "stream_copy_GB_s": round(stream_gbs, 1),
         "kernel_source_sha256_16": source_digest(),
     }
     del x, dual_out, mx9_out, y

@@ -17,7 +17,8 @@
 // in one fused multiply-add with 1.5 * 2^23 (its reciprocal is a normal
 // float for every block whose exponent byte is at least 9; smaller blocks
 // form it exactly with v_ldexp_f32), and clamped with one median.  A lane of
-// the flat pack issues eight 16-byte loads before it quantizes any of them.
+// the flat pack issues eight (large calls) or four 16-byte loads before it
+// quantizes any of them.
 //
 // Cache policy of the flat kernels (each byte is touched once): the pack
 // reads its input and writes q with the non-temporal hint, the unpack writes
@@ -116,8 +117,12 @@ void mx9_pack_any(const void* __restrict__ xv, int64_t ld_x, int64_t cols, uint3
 
 // Groups of 64 / kLanes blocks (one wave-wide 1 KiB load) that one wave of
 // the flat pack takes; their loads are all issued before the first group is
-// quantized.
-constexpr int kPackGroups = 8;
+// quantized.  Eight groups when that still leaves kPackWideMinWgs workgroups,
+// four otherwise (fewer, longer workgroups leave a larger share of the last
+// round idle).  Measured on MI355X: bf16 [32768, 8192] 127 us with eight, 129
+// us with four; the [4096, 14336] weights 47.5 us (fp32) and 29.9 us (bf16)
+// with four, 49.5 us and 31.0 us with eight.
+constexpr uint64_t kPackWideMinWgs = 8192;
 
 // Quantize one loaded 16-byte piece (this lane's share of block blk) and store
 // its outputs: q with the non-temporal hint, the max_exp and prime bytes with
@@ -138,12 +143,12 @@ __device__ __forceinline__ void pack_piece_store(uint4 d, uint64_t blk, uint32_t
 // kDtype 0: fp32, 4 lanes x 4 elements per block.  1: bf16, 2 lanes x 8.
 // Each wave owns kPackGroups groups of 64 / kLanes consecutive blocks; group k
 // is one contiguous 1 KiB load.  A lane issues its kPackGroups streaming loads
-// before it quantizes anything, so a wave keeps 8 KiB of reads in flight.
+// before it quantizes anything, so a wave keeps up to 8 KiB of reads in flight.
 // Measured on MI355X (bf16 [32768, 8192], rotating buffers): one group per
 // wave 157 us, two 133 us, eight 127 us; in the cast -> pack -> unpack
 // sequence the step went from 471 us to 452 us.  Streaming the max_exp and
 // prime bytes as well costs 4% (one group) to 7% (two groups) in the step.
-template <int kDtype>
+template <int kDtype, int kPackGroups>
 __global__ __launch_bounds__(kThreads)
 void mx9_pack_flat(const void* __restrict__ xv, uint64_t nb, int8_t* __restrict__ q,
                    uint8_t* __restrict__ max_exp, uint8_t* __restrict__ prime) {
@@ -284,11 +289,18 @@ hipError_t launch_mx9_pack(const void* x, int dtype, int64_t rows, int64_t cols,
     const dim3 grid(uint32_t((nb + kThreads - 1) / kThreads));
     const bool vec = cols % 16 == 0 && aligned16(x) && (ld_x * esz) % 16 == 0;
     if (vec && ld_x == cols && aligned16(q)) {
-        // kPackGroups * 64 / kLanes blocks per wave, 4 waves per workgroup
-        const uint64_t per_wg = uint64_t(kThreads / 64) * kPackGroups * (dtype == 0 ? 16 : 32);
+        // groups * 64 / kLanes blocks per wave, 4 waves per workgroup
+        const uint64_t per_group_wg = uint64_t(kThreads / 64) * (dtype == 0 ? 16 : 32);
+        const bool wide = (nb + 8 * per_group_wg - 1) / (8 * per_group_wg) >= kPackWideMinWgs;
+        const uint64_t per_wg = per_group_wg * (wide ? 8 : 4);
         const dim3 fgrid(uint32_t((nb + per_wg - 1) / per_wg));
-        if (dtype == 0) hipLaunchKernelGGL(mx9_pack_flat<0>, fgrid, dim3(kThreads), 0, stream, x, nb, q, max_exp, prime);
-        else hipLaunchKernelGGL(mx9_pack_flat<1>, fgrid, dim3(kThreads), 0, stream, x, nb, q, max_exp, prime);
+        if (dtype == 0) {
+            if (wide) hipLaunchKernelGGL((mx9_pack_flat<0, 8>), fgrid, dim3(kThreads), 0, stream, x, nb, q, max_exp, prime);
+            else hipLaunchKernelGGL((mx9_pack_flat<0, 4>), fgrid, dim3(kThreads), 0, stream, x, nb, q, max_exp, prime);
+        } else {
+            if (wide) hipLaunchKernelGGL((mx9_pack_flat<1, 8>), fgrid, dim3(kThreads), 0, stream, x, nb, q, max_exp, prime);
+            else hipLaunchKernelGGL((mx9_pack_flat<1, 4>), fgrid, dim3(kThreads), 0, stream, x, nb, q, max_exp, prime);
+        }
         return hipGetLastError();
     }
     if (dtype == 0) {

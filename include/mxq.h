@@ -207,6 +207,36 @@ int mx9_unpack(const int8_t *q, const uint8_t *max_exp, const uint8_t *prime,
                void *y, int64_t ld_y, void *stream);
 
 /*
+ * mx9_pack_strided -- mx9_pack writing each of its three outputs at a row
+ * pitch of the caller's choice ([MX9], review comments on the output offsets,
+ * which ask why the output tensors take no strides).  Same blocks, same
+ * bytes as mx9_pack; only where row r's bytes go changes:
+ *
+ *   q        block j of row r at q + r * ld_q + 16 j   (ld_q in bytes, a
+ *            multiple of 16 and >= 16 * ceil(cols/16)),
+ *   max_exp  at max_exp + r * ld_e + j                 (ld_e >= ceil(cols/16)),
+ *   prime    at prime + r * ld_pr + j                  (ld_pr >= ceil(cols/16)).
+ *
+ * Bytes between the rows' used ranges are not written.  mx9_pack is this call
+ * with ld_q = 16 * ceil(cols/16) and ld_e = ld_pr = ceil(cols/16).
+ * Errors as for mx9_pack, plus MX_E_STRIDE for a pitch below its row or an ld_q
+ * that is not a multiple of 16; the byte ranges spanned by the three pitched
+ * outputs take part in the overlap check.
+ */
+int mx9_pack_strided(const void *x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                     int32_t block_size, int8_t *q, int64_t ld_q, uint8_t *max_exp, int64_t ld_e,
+                     uint8_t *prime, int64_t ld_pr, void *stream);
+
+/*
+ * mx9_unpack_strided -- mx9_unpack reading q, max_exp and prime at the row
+ * pitches of mx9_pack_strided.  Errors as for mx9_unpack, plus the pitch
+ * checks of mx9_pack_strided.
+ */
+int mx9_unpack_strided(const int8_t *q, int64_t ld_q, const uint8_t *max_exp, int64_t ld_e,
+                       const uint8_t *prime, int64_t ld_pr, int64_t rows, int64_t cols,
+                       int32_t block_size, int32_t out_dtype, void *y, int64_t ld_y, void *stream);
+
+/*
  * mx9_pack_axis -- MX9 pack in blocks of 16 along any axis ([MX9], the
  * calls' axis argument; the shape and the axis are not stored, so the caller
  * passes them back to the unpack).

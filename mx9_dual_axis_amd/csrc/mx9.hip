@@ -42,15 +42,26 @@ constexpr int kThreads = 256;
 
 
 
+// Where the per-block kernels put block j of row r: q bytes at
+// q + r * ld_q + 16 j (ld_q a multiple of 16), the exponent byte at
+// max_exp + r * ld_e + j, the prime byte at prime + r * ld_pr + j.  The
+// contiguous three-part form is ld_q = 16 * blocks_per_row, ld_e = ld_pr =
+// blocks_per_row.
+struct Mx9Pitch {
+    int64_t q, e, pr;
+};
+
 // Vector path: cols % 16 == 0 and 16-byte aligned block starts.
 template <int kDtype>
 __global__ __launch_bounds__(kThreads)
 void mx9_pack_vec(const void* __restrict__ xv, int64_t ld_x, uint32_t blocks_per_row, uint64_t nb,
-                  int8_t* __restrict__ q, uint8_t* __restrict__ max_exp, uint8_t* __restrict__ prime) {
+                  int8_t* __restrict__ q, uint8_t* __restrict__ max_exp, uint8_t* __restrict__ prime,
+                  Mx9Pitch ld) {
     const uint64_t blk = uint64_t(blockIdx.x) * kThreads + threadIdx.x;
     if (blk >= nb) return;
     const uint64_t row = blk / blocks_per_row;
-    const uint64_t col = (blk - row * blocks_per_row) * 16;
+    const uint64_t jb = blk - row * blocks_per_row;
+    const uint64_t col = jb * 16;
     uint32_t w[16];
     if (kDtype == 0) {
         const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(xv) + row * ld_x + col);
@@ -74,9 +85,9 @@ void mx9_pack_vec(const void* __restrict__ xv, int64_t ld_x, uint32_t blocks_per
     }
     uint32_t qd[4], me, pr;
     pack16(w, qd, me, pr);
-    reinterpret_cast<uint4*>(q)[blk] = make_uint4(qd[0], qd[1], qd[2], qd[3]);
-    max_exp[blk] = uint8_t(me);
-    prime[blk] = uint8_t(pr);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(q) + row * ld.q + col) = make_uint4(qd[0], qd[1], qd[2], qd[3]);
+    max_exp[row * ld.e + jb] = uint8_t(me);
+    prime[row * ld.pr + jb] = uint8_t(pr);
 }
 
 // General path: any cols (trailing partial block padded with +0), any ld_x.
@@ -84,11 +95,12 @@ template <int kDtype>
 __global__ __launch_bounds__(kThreads)
 void mx9_pack_any(const void* __restrict__ xv, int64_t ld_x, int64_t cols, uint32_t blocks_per_row,
                   uint64_t nb, int8_t* __restrict__ q, uint8_t* __restrict__ max_exp,
-                  uint8_t* __restrict__ prime) {
+                  uint8_t* __restrict__ prime, Mx9Pitch ld) {
     const uint64_t blk = uint64_t(blockIdx.x) * kThreads + threadIdx.x;
     if (blk >= nb) return;
     const uint64_t row = blk / blocks_per_row;
-    const int64_t col = int64_t(blk - row * blocks_per_row) * 16;
+    const uint64_t jb = blk - row * blocks_per_row;
+    const int64_t col = int64_t(jb) * 16;
     uint32_t w[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -102,9 +114,9 @@ void mx9_pack_any(const void* __restrict__ xv, int64_t ld_x, int64_t cols, uint3
     }
     uint32_t qd[4], me, pr;
     pack16(w, qd, me, pr);
-    reinterpret_cast<uint4*>(q)[blk] = make_uint4(qd[0], qd[1], qd[2], qd[3]);
-    max_exp[blk] = uint8_t(me);
-    prime[blk] = uint8_t(pr);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(q) + row * ld.q + jb * 16) = make_uint4(qd[0], qd[1], qd[2], qd[3]);
+    max_exp[row * ld.e + jb] = uint8_t(me);
+    prime[row * ld.pr + jb] = uint8_t(pr);
 }
 
 // ---------------------------------------------------------------------------
@@ -236,14 +248,15 @@ template <int kOut, bool kVec>
 __global__ __launch_bounds__(kThreads)
 void mx9_unpack_kernel(const int8_t* __restrict__ q, const uint8_t* __restrict__ max_exp,
                        const uint8_t* __restrict__ prime, int64_t cols, uint32_t blocks_per_row,
-                       uint64_t nb, void* __restrict__ yv, int64_t ld_y) {
+                       uint64_t nb, void* __restrict__ yv, int64_t ld_y, Mx9Pitch ld) {
     const uint64_t blk = uint64_t(blockIdx.x) * kThreads + threadIdx.x;
     if (blk >= nb) return;
     const uint64_t row = blk / blocks_per_row;
-    const int64_t col = int64_t(blk - row * blocks_per_row) * 16;
-    const uint4 qv = reinterpret_cast<const uint4*>(q)[blk];
-    const uint32_t S = max_exp[blk];
-    const uint32_t pr = prime[blk];
+    const uint64_t jb = blk - row * blocks_per_row;
+    const int64_t col = int64_t(jb) * 16;
+    const uint4 qv = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(q) + row * ld.q + jb * 16);
+    const uint32_t S = max_exp[row * ld.e + jb];
+    const uint32_t pr = prime[row * ld.pr + jb];
     float y[16];
     unpack16(qv, S, pr, y);
     if (kOut == 0) {
@@ -282,13 +295,16 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 }  // namespace
 
 hipError_t launch_mx9_pack(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
-                           int8_t* q, uint8_t* max_exp, uint8_t* prime, hipStream_t stream) {
+                           int8_t* q, int64_t ld_q, uint8_t* max_exp, int64_t ld_e, uint8_t* prime,
+                           int64_t ld_pr, hipStream_t stream) {
     const int64_t esz = dtype == 0 ? 4 : 2;
     const uint32_t bpr = uint32_t((cols + 15) / 16);
     const uint64_t nb = uint64_t(rows) * bpr;
     const dim3 grid(uint32_t((nb + kThreads - 1) / kThreads));
     const bool vec = cols % 16 == 0 && aligned16(x) && (ld_x * esz) % 16 == 0;
-    if (vec && ld_x == cols && aligned16(q)) {
+    const bool packed_out = (ld_q == 16 * int64_t(bpr) && ld_e == int64_t(bpr) && ld_pr == int64_t(bpr)) || rows == 1;
+    const Mx9Pitch ld{ld_q, ld_e, ld_pr};
+    if (vec && ld_x == cols && aligned16(q) && packed_out) {
         // groups * 64 / kLanes blocks per wave, 4 waves per workgroup
         const uint64_t per_group_wg = uint64_t(kThreads / 64) * (dtype == 0 ? 16 : 32);
         const bool wide = (nb + 8 * per_group_wg - 1) / (8 * per_group_wg) >= kPackWideMinWgs;
@@ -304,35 +320,37 @@ hipError_t launch_mx9_pack(const void* x, int dtype, int64_t rows, int64_t cols,
         return hipGetLastError();
     }
     if (dtype == 0) {
-        if (vec) hipLaunchKernelGGL(mx9_pack_vec<0>, grid, dim3(kThreads), 0, stream, x, ld_x, bpr, nb, q, max_exp, prime);
-        else hipLaunchKernelGGL(mx9_pack_any<0>, grid, dim3(kThreads), 0, stream, x, ld_x, cols, bpr, nb, q, max_exp, prime);
+        if (vec) hipLaunchKernelGGL(mx9_pack_vec<0>, grid, dim3(kThreads), 0, stream, x, ld_x, bpr, nb, q, max_exp, prime, ld);
+        else hipLaunchKernelGGL(mx9_pack_any<0>, grid, dim3(kThreads), 0, stream, x, ld_x, cols, bpr, nb, q, max_exp, prime, ld);
     } else {
-        if (vec) hipLaunchKernelGGL(mx9_pack_vec<1>, grid, dim3(kThreads), 0, stream, x, ld_x, bpr, nb, q, max_exp, prime);
-        else hipLaunchKernelGGL(mx9_pack_any<1>, grid, dim3(kThreads), 0, stream, x, ld_x, cols, bpr, nb, q, max_exp, prime);
+        if (vec) hipLaunchKernelGGL(mx9_pack_vec<1>, grid, dim3(kThreads), 0, stream, x, ld_x, bpr, nb, q, max_exp, prime, ld);
+        else hipLaunchKernelGGL(mx9_pack_any<1>, grid, dim3(kThreads), 0, stream, x, ld_x, cols, bpr, nb, q, max_exp, prime, ld);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_mx9_unpack(const int8_t* q, const uint8_t* max_exp, const uint8_t* prime,
-                             int64_t rows, int64_t cols, int out_dtype, void* y, int64_t ld_y,
-                             hipStream_t stream) {
+hipError_t launch_mx9_unpack(const int8_t* q, int64_t ld_q, const uint8_t* max_exp, int64_t ld_e,
+                             const uint8_t* prime, int64_t ld_pr, int64_t rows, int64_t cols, int out_dtype,
+                             void* y, int64_t ld_y, hipStream_t stream) {
     const int64_t esz = out_dtype == 0 ? 4 : 2;
     const uint32_t bpr = uint32_t((cols + 15) / 16);
     const uint64_t nb = uint64_t(rows) * bpr;
     const dim3 grid(uint32_t((nb + kThreads - 1) / kThreads));
     const bool vec = cols % 16 == 0 && aligned16(y) && (ld_y * esz) % 16 == 0;
-    if (vec && ld_y == cols && aligned16(q)) {
+    const bool packed_in = (ld_q == 16 * int64_t(bpr) && ld_e == int64_t(bpr) && ld_pr == int64_t(bpr)) || rows == 1;
+    const Mx9Pitch ld{ld_q, ld_e, ld_pr};
+    if (vec && ld_y == cols && aligned16(q) && packed_in) {
         const dim3 fgrid(uint32_t((nb + 255) / 256));
         if (out_dtype == 0) hipLaunchKernelGGL(mx9_unpack_flat<0>, fgrid, dim3(kThreads), 0, stream, q, max_exp, prime, nb, y);
         else hipLaunchKernelGGL(mx9_unpack_flat<1>, fgrid, dim3(kThreads), 0, stream, q, max_exp, prime, nb, y);
         return hipGetLastError();
     }
     if (out_dtype == 0) {
-        if (vec) hipLaunchKernelGGL((mx9_unpack_kernel<0, true>), grid, dim3(kThreads), 0, stream, q, max_exp, prime, cols, bpr, nb, y, ld_y);
-        else hipLaunchKernelGGL((mx9_unpack_kernel<0, false>), grid, dim3(kThreads), 0, stream, q, max_exp, prime, cols, bpr, nb, y, ld_y);
+        if (vec) hipLaunchKernelGGL((mx9_unpack_kernel<0, true>), grid, dim3(kThreads), 0, stream, q, max_exp, prime, cols, bpr, nb, y, ld_y, ld);
+        else hipLaunchKernelGGL((mx9_unpack_kernel<0, false>), grid, dim3(kThreads), 0, stream, q, max_exp, prime, cols, bpr, nb, y, ld_y, ld);
     } else {
-        if (vec) hipLaunchKernelGGL((mx9_unpack_kernel<1, true>), grid, dim3(kThreads), 0, stream, q, max_exp, prime, cols, bpr, nb, y, ld_y);
-        else hipLaunchKernelGGL((mx9_unpack_kernel<1, false>), grid, dim3(kThreads), 0, stream, q, max_exp, prime, cols, bpr, nb, y, ld_y);
+        if (vec) hipLaunchKernelGGL((mx9_unpack_kernel<1, true>), grid, dim3(kThreads), 0, stream, q, max_exp, prime, cols, bpr, nb, y, ld_y, ld);
+        else hipLaunchKernelGGL((mx9_unpack_kernel<1, false>), grid, dim3(kThreads), 0, stream, q, max_exp, prime, cols, bpr, nb, y, ld_y, ld);
     }
     return hipGetLastError();
 }

@@ -681,7 +681,8 @@ void launch_unpack_records_rows(const uint8_t* packed, int64_t ld_p, int64_t row
 hipError_t launch_mx9_pack_axis(const void* x, int dtype, int64_t outer, int64_t len, int64_t inner,
                                 int8_t* q, uint8_t* max_exp, uint8_t* prime, hipStream_t stream) {
     if (inner == 1)   // the last axis: rows of len elements
-        return launch_mx9_pack(x, dtype, outer, len, len, q, max_exp, prime, stream);
+        return launch_mx9_pack(x, dtype, outer, len, len, q, 16 * ((len + 15) / 16), max_exp, (len + 15) / 16, prime,
+                               (len + 15) / 16, stream);
     launch_pack_tiles<false>(x, dtype, outer, len, inner, q, max_exp, prime, nullptr, 0, stream);
     return hipGetLastError();
 }
@@ -690,7 +691,8 @@ hipError_t launch_mx9_unpack_axis(const int8_t* q, const uint8_t* max_exp, const
                                   int64_t outer, int64_t len, int64_t inner, int out_dtype, void* y,
                                   hipStream_t stream) {
     if (inner == 1)
-        return launch_mx9_unpack(q, max_exp, prime, outer, len, out_dtype, y, len, stream);
+        return launch_mx9_unpack(q, 16 * ((len + 15) / 16), max_exp, (len + 15) / 16, prime, (len + 15) / 16, outer, len,
+                                 out_dtype, y, len, stream);
     launch_unpack_tiles<false>(q, max_exp, prime, nullptr, 0, outer, len, inner, out_dtype, y, stream);
     return hipGetLastError();
 }

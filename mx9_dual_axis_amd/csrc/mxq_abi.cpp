@@ -293,52 +293,79 @@ int mx_quantize_grouped_mfma(const uint16_t* x, int64_t M, int64_t N, int64_t ld
                         true, stream);
 }
 
-int mx9_pack(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld_x,
-             int32_t block_size, int8_t* q, uint8_t* max_exp, uint8_t* prime, void* stream) {
+int mx9_pack_strided(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                     int32_t block_size, int8_t* q, int64_t ld_q, uint8_t* max_exp, int64_t ld_e,
+                     uint8_t* prime, int64_t ld_pr, void* stream) {
     const bool empty = rows == 0 || cols == 0;   // empty buffers may be NULL
     if (!empty && (!x || !q || !max_exp || !prime)) return MX_E_NULL;
     if (dtype != MX_DTYPE_F32 && dtype != MX_DTYPE_BF16) return MX_E_DTYPE;
     if (block_size != 16) return MX_E_BLOCK;
     if (rows < 0 || cols < 0 || rows > (int64_t(1) << 40) || cols > kMaxDim) return MX_E_SHAPE;
-    const uint64_t nb = uint64_t(rows) * uint64_t((cols + 15) / 16);
+    const int64_t bpr = (cols + 15) / 16;
+    const uint64_t nb = uint64_t(rows) * uint64_t(bpr);
     if (nb > kMaxThreads) return MX_E_SHAPE;
     if (ld_x < cols || ld_x > (int64_t(1) << 40)) return MX_E_STRIDE;
+    if (ld_q < 16 * bpr || ld_q % 16 != 0 || ld_e < bpr || ld_pr < bpr || ld_q > (int64_t(1) << 40) ||
+        ld_e > (int64_t(1) << 40) || ld_pr > (int64_t(1) << 40))
+        return MX_E_STRIDE;
     const int64_t esz = dtype == MX_DTYPE_F32 ? 4 : 2;
     const uint64_t xb = matrix_bytes(rows, cols, ld_x, esz);
-    if (xb == kTooLarge) return MX_E_STRIDE;
+    const uint64_t qb = matrix_bytes(rows, 16 * bpr, ld_q, 1);
+    const uint64_t eb = matrix_bytes(rows, bpr, ld_e, 1);
+    const uint64_t pb = matrix_bytes(rows, bpr, ld_pr, 1);
+    if (xb == kTooLarge || qb == kTooLarge || eb == kTooLarge || pb == kTooLarge) return MX_E_STRIDE;
     if (!empty && (!aligned(x, uintptr_t(esz)) || !aligned(q, 16))) return MX_E_ALIGN;
-    const Span s[4] = {{addr(x), xb}, {addr(q), nb * 16},
-                       {addr(max_exp), nb}, {addr(prime), nb}};
+    const Span s[4] = {{addr(x), xb}, {addr(q), qb}, {addr(max_exp), eb}, {addr(prime), pb}};
     if (any_overlap(s, 4)) return MX_E_OVERLAP;
     if (nb == 0) return MX_OK;
-    hipError_t e = mxq::launch_mx9_pack(x, dtype, rows, cols, ld_x, q, max_exp, prime,
+    hipError_t e = mxq::launch_mx9_pack(x, dtype, rows, cols, ld_x, q, ld_q, max_exp, ld_e, prime, ld_pr,
                                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
 }
 
-int mx9_unpack(const int8_t* q, const uint8_t* max_exp, const uint8_t* prime,
-               int64_t rows, int64_t cols, int32_t block_size, int32_t out_dtype,
-               void* y, int64_t ld_y, void* stream) {
+int mx9_unpack_strided(const int8_t* q, int64_t ld_q, const uint8_t* max_exp, int64_t ld_e,
+                       const uint8_t* prime, int64_t ld_pr, int64_t rows, int64_t cols, int32_t block_size,
+                       int32_t out_dtype, void* y, int64_t ld_y, void* stream) {
     const bool empty = rows == 0 || cols == 0;   // empty buffers may be NULL
     if (!empty && (!q || !max_exp || !prime || !y)) return MX_E_NULL;
     if (out_dtype != MX_DTYPE_F32 && out_dtype != MX_DTYPE_BF16) return MX_E_DTYPE;
     if (block_size != 16) return MX_E_BLOCK;
     if (rows < 0 || cols < 0 || rows > (int64_t(1) << 40) || cols > kMaxDim) return MX_E_SHAPE;
-    const uint64_t nb = uint64_t(rows) * uint64_t((cols + 15) / 16);
+    const int64_t bpr = (cols + 15) / 16;
+    const uint64_t nb = uint64_t(rows) * uint64_t(bpr);
     if (nb > kMaxThreads) return MX_E_SHAPE;
     if (ld_y < cols || ld_y > (int64_t(1) << 40)) return MX_E_STRIDE;
+    if (ld_q < 16 * bpr || ld_q % 16 != 0 || ld_e < bpr || ld_pr < bpr || ld_q > (int64_t(1) << 40) ||
+        ld_e > (int64_t(1) << 40) || ld_pr > (int64_t(1) << 40))
+        return MX_E_STRIDE;
     const int64_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
     const uint64_t yb = matrix_bytes(rows, cols, ld_y, esz);
-    if (yb == kTooLarge) return MX_E_STRIDE;
+    const uint64_t qb = matrix_bytes(rows, 16 * bpr, ld_q, 1);
+    const uint64_t eb = matrix_bytes(rows, bpr, ld_e, 1);
+    const uint64_t pb = matrix_bytes(rows, bpr, ld_pr, 1);
+    if (yb == kTooLarge || qb == kTooLarge || eb == kTooLarge || pb == kTooLarge) return MX_E_STRIDE;
     if (!empty && (!aligned(q, 16) || !aligned(y, uintptr_t(esz)))) return MX_E_ALIGN;
-    const Span s[4] = {{addr(q), nb * 16}, {addr(max_exp), nb}, {addr(prime), nb}, {addr(y), yb}};
+    const Span s[4] = {{addr(q), qb}, {addr(max_exp), eb}, {addr(prime), pb}, {addr(y), yb}};
     if (any_overlap(s, 4)) return MX_E_OVERLAP;
     if (nb == 0) return MX_OK;
-    hipError_t e = mxq::launch_mx9_unpack(q, max_exp, prime, rows, cols, out_dtype, y, ld_y,
+    hipError_t e = mxq::launch_mx9_unpack(q, ld_q, max_exp, ld_e, prime, ld_pr, rows, cols, out_dtype, y, ld_y,
                                           static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MX_OK : MX_E_LAUNCH;
 }
 
+int mx9_pack(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld_x,
+             int32_t block_size, int8_t* q, uint8_t* max_exp, uint8_t* prime, void* stream) {
+    const int64_t bpr = cols > 0 && cols <= kMaxDim ? (cols + 15) / 16 : 0;   // others: MX_E_SHAPE
+    return mx9_pack_strided(x, dtype, rows, cols, ld_x, block_size, q, 16 * bpr, max_exp, bpr, prime, bpr, stream);
+}
+
+int mx9_unpack(const int8_t* q, const uint8_t* max_exp, const uint8_t* prime,
+               int64_t rows, int64_t cols, int32_t block_size, int32_t out_dtype,
+               void* y, int64_t ld_y, void* stream) {
+    const int64_t bpr = cols > 0 && cols <= kMaxDim ? (cols + 15) / 16 : 0;   // others: MX_E_SHAPE
+    return mx9_unpack_strided(q, 16 * bpr, max_exp, bpr, prime, bpr, rows, cols, block_size, out_dtype, y, ld_y,
+                              stream);
+}
 
 int mx9_pack_axis(const void* x, int32_t dtype, int64_t outer, int64_t len, int64_t inner,
                   int32_t block_size, int8_t* q, uint8_t* max_exp, uint8_t* prime, void* stream) {

@@ -22,13 +22,18 @@ hipError_t launch_offs_validate(const int32_t* offs, int32_t G, int64_t M, int32
                                 hipStream_t stream);
 
 // MX9 pack of [rows, cols] (rows, cols > 0); dtype 0 = fp32, 1 = bf16.
+// Row r's blocks go to q + r * ld_q (bytes, a multiple of 16), max_exp +
+// r * ld_e and prime + r * ld_pr; the three-part form passes ld_q = 16 *
+// ceil(cols/16) and ld_e = ld_pr = ceil(cols/16).
 hipError_t launch_mx9_pack(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
-                           int8_t* q, uint8_t* max_exp, uint8_t* prime, hipStream_t stream);
+                           int8_t* q, int64_t ld_q, uint8_t* max_exp, int64_t ld_e, uint8_t* prime,
+                           int64_t ld_pr, hipStream_t stream);
 
-// MX9 unpack to [rows, cols] (rows, cols > 0); out_dtype 0 = fp32, 1 = bf16.
-hipError_t launch_mx9_unpack(const int8_t* q, const uint8_t* max_exp, const uint8_t* prime,
-                             int64_t rows, int64_t cols, int out_dtype, void* y, int64_t ld_y,
-                             hipStream_t stream);
+// MX9 unpack to [rows, cols] (rows, cols > 0); out_dtype 0 = fp32, 1 = bf16;
+// the parts are read with the pitches of launch_mx9_pack.
+hipError_t launch_mx9_unpack(const int8_t* q, int64_t ld_q, const uint8_t* max_exp, int64_t ld_e,
+                             const uint8_t* prime, int64_t ld_pr, int64_t rows, int64_t cols, int out_dtype,
+                             void* y, int64_t ld_y, hipStream_t stream);
 
 // MX9 in blocks of 16 along the middle axis of a contiguous [outer, len,
 // inner] array (all > 0), blocks numbered (o * inner + i) * ceil(len/16) + j.

@@ -180,18 +180,41 @@ def mxfp8_grouped(x: np.ndarray, offs, threads: int = 1):
     rc = offs_check(offs, M)
     if rc != 0:
         return rc, None
+    ld = x.strides[0] // 2
+    q_row = np.empty((M, N), np.uint8)
+    s_row = np.empty((M, N // 32), np.uint8)
+    q_col = np.empty((N, M), np.uint8)
+    s_col = np.empty((M // 32, N), np.uint8)
+    lib = _load()
     if threads <= 1:
-        q_row = np.empty((M, N), np.uint8)
-        s_row = np.empty((M, N // 32), np.uint8)
-        q_col = np.empty((N, M), np.uint8)
-        s_col = np.empty((M // 32, N), np.uint8)
-        rc = _load().oref_mxfp8_grouped(_ptr(x), M, N, x.strides[0] // 2, _ptr(offs), len(offs),
-                                        _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col))
+        rc = lib.oref_mxfp8_grouped(_ptr(x), M, N, ld, _ptr(offs), len(offs),
+                                    _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col))
         return rc, (q_row, s_row, q_col, s_col)
-    # threaded: the dense cast by row slabs, then the tail rule of the C oracle
-    q_row, s_row, q_col, s_col = mxfp8_dual(x, threads)
-    covered = int(offs[-1]) if len(offs) else M
-    s_col[covered // 32:, :] = 0
+    # Threaded: every slab of rows [r0, r1) goes through the C grouped call on
+    # its own, with the group ends expressed relative to r0 and clipped to the
+    # slab.  Slabs start at multiples of 128, so the rebased ends stay valid
+    # multiples of 128, and a slab's uncovered rows are exactly the matrix's
+    # uncovered rows that fall in it; the tail rule itself is the C oracle's.
+    units = M // 128
+    slabs = [(128 * a, 128 * b) for a, b in _splits(units, threads)] if units else []
+    if slabs:
+        slabs[-1] = (slabs[-1][0], M)
+    elif M:
+        slabs = [(0, M)]
+    codes = []
+
+    def job(r0, r1):
+        def run():
+            local = np.clip(offs.astype(np.int64) - r0, 0, r1 - r0).astype(np.int32)
+            qt = np.empty((N, r1 - r0), np.uint8)
+            codes.append(lib.oref_mxfp8_grouped(_ptr(x) + r0 * ld * 2, r1 - r0, N, ld, _ptr(local), len(local),
+                                                _ptr(q_row) + r0 * N, _ptr(s_row) + r0 * (N // 32), _ptr(qt),
+                                                _ptr(s_col) + (r0 // 32) * N))
+            q_col[:, r0:r1] = qt
+        return run
+    _run([job(a, b) for a, b in slabs], threads)
+    if any(codes):
+        raise AssertionError(f"oracle: a rebased slab of valid offsets was rejected ({codes})")
     return 0, (q_row, s_row, q_col, s_col)
 
 

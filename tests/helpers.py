@@ -1,4 +1,4 @@
-"""Helpers shared by the GPU tests: device transfer and oracle sampling."""
+"""Helpers shared by the GPU tests: device transfer and progress lines."""
 import numpy as np
 import torch
 
@@ -24,15 +24,3 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 def say(msg: str):
     print(msg, flush=True)
-
-
-def sample_rows(M: int, k: int, seed: int) -> np.ndarray:
-    g = np.random.default_rng(seed)
-    r = np.unique(np.concatenate([[0, M - 1], g.integers(0, M, k)]))
-    return r
-
-
-def sample_slabs(M: int, k: int, seed: int) -> np.ndarray:
-    """Indices of 32-row block rows, including the first and the last."""
-    g = np.random.default_rng(seed + 1)
-    return np.unique(np.concatenate([[0, M // 32 - 1], g.integers(0, M // 32, k)]))

@@ -24,6 +24,7 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["mx_quantize_2d_dual", "mx_quantize_grouped", "mx9_pack", "mx9_unpack",
+                                  "mx9_pack_strided", "mx9_unpack_strided",
                                   "mx9_pack_axis", "mx9_unpack_axis", "mx9_pack_records", "mx9_unpack_records",
                                   "mx_gemm_nt", "mx_grouped_gemm_rows", "mx_grouped_gemm_k", "mx_status_string",
                                   "mx_quantize_2d_dual_mfma", "mx_quantize_grouped_mfma", "mx_gemm_nt_mfma",
@@ -106,6 +107,25 @@ def test_mx9_validation_codes():
     # before anything else is computed from it (no 64-bit overflow)
     assert pack(rows=1 << 31, cols=1, ld=1 << 40) == 6 and unpack(rows=1 << 31, cols=1, ld=1 << 40) == 6
     assert pack(rows=1 << 20, cols=16, ld=1 << 29) == 6 and pack(rows=1 << 10, cols=16, ld=1 << 29, x=FAKE) == 8
+
+
+def test_mx9_strided_validation_codes():
+    lib = mxq.library()
+    # 4 rows of 64 columns: 4 blocks per row
+    def pack(ld_q=96, ld_e=8, ld_p=8, rows=4, x=FAKE, q=FAKE * 2, e=FAKE * 3, p=FAKE * 4, y=None):
+        return lib.mx9_pack_strided(x, 0, rows, 64, 64, 16, q, ld_q, e, ld_e, p, ld_p, None)
+
+    def unpack(ld_q=96, ld_e=8, ld_p=8, rows=4, y=FAKE * 5, q=FAKE * 2, e=FAKE * 3, p=FAKE * 4, x=None):
+        return lib.mx9_unpack_strided(q, ld_q, e, ld_e, p, ld_p, rows, 64, 16, 0, y, 64, None)
+    for f in (pack, unpack):
+        assert f(ld_q=48) == 6 and f(ld_q=72) == 6 and f(ld_e=3) == 6 and f(ld_p=2) == 6
+        assert f(ld_q=1 << 41) == 6
+        assert f(q=FAKE * 2 + 8) == 7
+        assert f(e=FAKE * 2 + 300) == 8            # max_exp rows inside q's pitched span
+        assert f(p=FAKE * 3 + 20) == 8             # prime inside max_exp's span
+        assert f(rows=0, x=None, y=None, q=None, e=None, p=None) == 0
+    # the pitched spans, not only the used bytes, take part in the overlap check
+    assert pack(ld_e=1 << 20, p=FAKE * 3 + (1 << 20)) == 8
 
 
 def test_mx9_axis_and_record_validation_codes():

@@ -8,7 +8,7 @@ import torch
 
 import mx9_dual_axis_amd as mxq
 import oracle
-from helpers import bf16_to_dev, host, require_gpu, sample_rows, sample_slabs, say
+from helpers import bf16_to_dev, host, require_gpu, say
 from mx9_dual_axis_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -237,90 +237,56 @@ def test_host_rejections():
         mxq.mx_quantize_2d_dual(x, out=(q_row, s_row, q_row, s_col))
     assert e.value.status == 8
     with pytest.raises(mxq.MXError) as e:   # output aliasing the input
-        mxq.mx_quantize_2d_dual(x, out=(x.view(torch.uint8)[:, :256], s_row, q_col, s_col))
+        mxq.mx_quantize_2d_dual(x, out=(x.view(torch.uint8).reshape(-1)[:65536].view(256, 256), s_row, q_col, s_col))
     assert e.value.status == 8
 
 
-# ---------------------------------------------------------------- full sizes
-
-@pytest.fixture(scope="module")
-def mixed_full():
-    say("generating the mixed-magnitude workload bf16 [8192, 7168] (seed 2)")
-    return synth.dual_mixed()
-
-
-@pytest.fixture(scope="module")
-def stress_full():
-    say("generating the stress workload bf16 [32768, 8192] (seed 5)")
-    return synth.stress()
-
-
-def _sampled_check(xb, got, tag, k_rows=48, k_slabs=6, seed=0):
-    M, N = xb.shape
-    q_row, s_row, q_col, s_col = (host(t) for t in got)
-    rows = sample_rows(M, k_rows, seed)
-    qr, sr = oracle.mxfp8_rowwise(np.ascontiguousarray(xb[rows]), threads=THREADS)
-    assert np.array_equal(q_row[rows], qr), f"{tag}: q_row rows"
-    assert np.array_equal(s_row[rows], sr), f"{tag}: s_row rows"
-    for i in sample_slabs(M, k_slabs, seed):
-        qc, sc = oracle.mxfp8_colwise(np.ascontiguousarray(xb[32 * i:32 * i + 32]), threads=THREADS)
-        assert np.array_equal(q_col[:, 32 * i:32 * i + 32], qc), f"{tag}: q_col slab {i}"
-        assert np.array_equal(s_col[i:i + 1], sc), f"{tag}: s_col slab {i}"
-
-
-def test_full_size_mixed_sampled(mixed_full):
+def test_caller_outputs_checked_before_launch():
+    """Caller-supplied outputs of the wrong device, dtype, shape or layout
+    raise in the binding; nothing is launched."""
     dev = require_gpu()
-    xb = mixed_full
-    say("full size [8192, 7168]: sampled parity, transposition, determinism")
-    xd = bf16_to_dev(xb)
-    out = _dirty_outputs(*xb.shape, dev)
+    say("binding checks of caller outputs")
+    x = torch.zeros((256, 128), dtype=torch.bfloat16, device=dev)
+    good = list(_dirty_outputs(256, 128, dev))
+    bad_cases = {
+        "host q_row": torch.zeros((256, 128), dtype=torch.uint8),
+        "short q_col": torch.zeros((128, 128), dtype=torch.uint8, device=dev),
+        "int8 s_row": torch.zeros((256, 4), dtype=torch.int8, device=dev),
+        "strided s_col": torch.zeros((8, 256), dtype=torch.uint8, device=dev)[:, ::2],
+    }
+    slots = {"host q_row": 0, "short q_col": 2, "int8 s_row": 1, "strided s_col": 3}
+    for name, t in bad_cases.items():
+        out = list(good)
+        out[slots[name]] = t
+        with pytest.raises(ValueError) as e:
+            mxq.mx_quantize_2d_dual(x, out=tuple(out))
+        assert not isinstance(e.value, mxq.MXError), name
+    with pytest.raises(ValueError):
+        mxq.mx_quantize_2d_dual(x, out=tuple(good[:3]))
+    with pytest.raises(ValueError):      # plain-layout buffers passed for the matrix-core layout
+        mxq.mx_quantize_2d_dual(x, out=tuple(good), scale_layout="mfma")
+    with pytest.raises(ValueError):
+        mxq.mx_quantize_grouped(x, torch.zeros(1, dtype=torch.int32), out=tuple(good))
+    for o in good:                       # untouched
+        assert int((o != 0xA5).sum()) == 0
+
+
+# ---------------------------------------------------------------- full sizes
+# Every output byte of the workloads at full size is compared with the
+# oracle in test_gpu_full_size.py; here, properties of the full-size call.
+
+def test_full_size_mixed_properties():
+    """bf16 [8192, 7168]: for finite input the colwise outputs equal the
+    rowwise outputs of the transpose, and repeated calls give the same bytes."""
+    dev = require_gpu()
+    say("full size [8192, 7168]: transposition and determinism")
+    xd = bf16_to_dev(synth.dual_mixed())
+    out = _dirty_outputs(*xd.shape, dev)
     mxq.mx_quantize_2d_dual(xd, out=out)
-    torch.cuda.synchronize()
-    _sampled_check(xb, out, "mixed")
-    # finite input: colwise outputs equal the rowwise outputs of the transpose
     qr_t, sr_t, _, _ = mxq.mx_quantize_2d_dual(xd.t().contiguous())
     torch.cuda.synchronize()
     assert torch.equal(out[2], qr_t) and torch.equal(out[3], sr_t.t())
-    again = _dirty_outputs(*xb.shape, dev, 0x11)
+    again = _dirty_outputs(*xd.shape, dev, 0x11)
     mxq.mx_quantize_2d_dual(xd, out=again)
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip(out, again))
-
-
-def test_full_size_stress_sampled(stress_full):
-    dev = require_gpu()
-    xb = stress_full
-    say("full size [32768, 8192] stress: sampled parity (Inf/NaN, subnormal and near-max tiles)")
-    out = _dirty_outputs(*xb.shape, dev)
-    mxq.mx_quantize_2d_dual(bf16_to_dev(xb), out=out)
-    torch.cuda.synchronize()
-    # make sure the sample holds the special rows: every row/slab containing Inf or NaN
-    special = np.argwhere((xb & 0x7F80) == 0x7F80)
-    rows = np.unique(special[:, 0])
-    got = [host(t) for t in out]
-    qr, sr = oracle.mxfp8_rowwise(np.ascontiguousarray(xb[rows]), threads=THREADS)
-    assert np.array_equal(got[0][rows], qr) and np.array_equal(got[1][rows], sr)
-    for i in np.unique(rows // 32)[:64]:
-        qc, sc = oracle.mxfp8_colwise(np.ascontiguousarray(xb[32 * i:32 * i + 32]), threads=THREADS)
-        assert np.array_equal(got[2][:, 32 * i:32 * i + 32], qc), f"slab {i}"
-        assert np.array_equal(got[3][i:i + 1], sc)
-    _sampled_check(xb, out, "stress", seed=5)
-
-
-def test_full_size_grouped():
-    dev = require_gpu()
-    say("full size grouped [16384, 5120], 64 groups, covered 12288")
-    xb, offs = synth.grouped()
-    assert offs[-1] == 12288
-    xd = bf16_to_dev(xb)
-    err = torch.full((1,), -7, dtype=torch.int32, device=dev)
-    out = _dirty_outputs(*xb.shape, dev)
-    mxq.mx_quantize_grouped(xd, torch.from_numpy(offs).to(dev), err=err, out=out)
-    dense = mxq.mx_quantize_2d_dual(xd)
-    torch.cuda.synchronize()
-    assert int(err.item()) == 0
-    for a, b in zip(out[:3], dense[:3]):
-        assert torch.equal(a, b)
-    assert torch.equal(out[3][:12288 // 32], dense[3][:12288 // 32])
-    assert int(out[3][12288 // 32:].count_nonzero()) == 0
-    _sampled_check(xb, dense, "grouped-dense", seed=3)

@@ -8,7 +8,7 @@ import torch
 
 import mx9_dual_axis_amd as mxq
 import oracle
-from helpers import bf16_to_dev, host, require_gpu, sample_rows, say
+from helpers import bf16_to_dev, host, require_gpu, say
 from mx9_dual_axis_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -189,6 +189,29 @@ def test_rejections_and_empty():
     with pytest.raises(mxq.MXError) as ei:
         mxq.mx9_unpack(q, e, p, 4, 16, out_dtype=torch.float16)
     assert ei.value.status == 2
+    # caller outputs and inputs: wrong device, dtype, size or layout raise in the binding
+    x = torch.zeros((4, 32), dtype=torch.float32, device=dev)
+    good = (torch.zeros((8, 16), dtype=torch.int8, device=dev), torch.zeros((8,), dtype=torch.uint8, device=dev),
+            torch.zeros((8, 1), dtype=torch.uint8, device=dev))
+    for k, bad in ((0, torch.zeros((8, 16), dtype=torch.int8)),                   # host
+                   (0, torch.zeros((7, 16), dtype=torch.int8, device=dev)),       # too small
+                   (1, torch.zeros((8,), dtype=torch.int8, device=dev)),          # dtype
+                   (2, torch.zeros((8, 2), dtype=torch.uint8, device=dev)[:, :1])):  # not contiguous
+        out = list(good)
+        out[k] = bad
+        with pytest.raises(ValueError) as ei:
+            mxq.mx9_pack(x, out=tuple(out))
+        assert not isinstance(ei.value, mxq.MXError)
+    with pytest.raises(ValueError):
+        mxq.mx9_unpack(good[0], good[1], good[2], 4, 32, out=torch.zeros((4, 32), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        mxq.mx9_unpack(good[0], good[1], good[2], 4, 32, out=torch.zeros((4, 32), dtype=torch.float16, device=dev))
+    with pytest.raises(ValueError):
+        mxq.mx9_unpack(good[0].cpu(), good[1], good[2], 4, 32)
+    with pytest.raises(ValueError):
+        mxq.mx9_pack_records(x, out=torch.zeros((4, 36), dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        mxq.mx9_unpack_axis(good[0], good[1], good[2], (4, 32), 1, out=torch.zeros((4, 32), device=dev).t())
     q, e, p = mxq.mx9_pack(torch.zeros((0, 16), dtype=torch.float32, device=dev))
     assert q.shape == (0, 16)
     y = mxq.mx9_unpack(q, e, p, 0, 16)
@@ -217,50 +240,61 @@ def test_graph_capture():
         assert np.array_equal(host(y), wy), rep
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("rows,cols", [(33, 200), (64, 1024), (1, 48), (130, 16)])
+def test_pitched_parts(dtype, rows, cols):
+    """mx9_pack_strided / mx9_unpack_strided: q, max_exp and prime as column
+    slices of wider tensors (each at its own row pitch) hold the oracle's
+    bytes in their used columns and leave the rest untouched; the unpack reads
+    them back at those pitches."""
+    dev = require_gpu()
+    say(f"mx9 pitched parts {dtype} [{rows}, {cols}]")
+    x = synth.mx9_weights(rows, cols, 7 * rows + cols, dtype)
+    nbr = (cols + 15) // 16
+    qw = torch.full((rows, 16 * nbr + 48), 0x5A, dtype=torch.int8, device=dev)
+    ew = torch.full((rows, nbr + 5), 0xA5, dtype=torch.uint8, device=dev)
+    pw = torch.full((rows, nbr + 9), 0xA5, dtype=torch.uint8, device=dev)
+    q, e, p = qw[:, 16:16 + 16 * nbr], ew[:, 3:3 + nbr], pw[:, :nbr]
+    mxq.mx9_pack_strided(_to_dev(x), out=(q, e, p))
+    torch.cuda.synchronize()
+    wq, we, wp = oracle.mx9_pack(x, threads=THREADS)
+    assert np.array_equal(host(q), wq.reshape(rows, 16 * nbr))
+    assert np.array_equal(host(e), we.reshape(rows, nbr))
+    assert np.array_equal(host(p), wp.reshape(rows, nbr))
+    hq, he, hp = host(qw), host(ew), host(pw)
+    assert (hq[:, :16] == 0x5A).all() and (hq[:, 16 + 16 * nbr:] == 0x5A).all()
+    assert (he[:, :3] == 0xA5).all() and (he[:, 3 + nbr:] == 0xA5).all() and (hp[:, nbr:] == 0xA5).all()
+    for od, td in (("fp32", torch.float32), ("bf16", torch.bfloat16)):
+        want = oracle.mx9_unpack(wq, we, wp, rows, cols, od)
+        yw = torch.full((rows, cols + 8), 3, dtype=td, device=dev)
+        mxq.mx9_unpack_strided(q, e, p, rows, cols, out=yw[:, :cols])
+        torch.cuda.synchronize()
+        got = host(yw)
+        bits = np.uint32 if od == "fp32" else np.uint16
+        assert np.array_equal(got[:, :cols].view(bits), want.view(bits)), od
+        assert bool((yw[:, cols:].float() == 3).all())
+    # the contiguous call is the special case with packed pitches
+    q2, e2, p2 = mxq.mx9_pack_strided(_to_dev(x))
+    assert np.array_equal(host(q2), wq.reshape(rows, 16 * nbr)) and np.array_equal(host(p2), wp.reshape(rows, nbr))
+
+
 # ---------------------------------------------------------------- full sizes
+# Every byte of the full-size workloads is compared with the oracle in
+# test_gpu_full_size.py; here, the round trip's quality at full size.
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_full_size_weights_sampled(dtype):
+def test_full_size_weights_snr(dtype):
+    """SNR of the [4096, 14336] weights' round trip (the page reports about
+    46 dB for clean data and about 42 dB with outliers; this mixture has a
+    heavy tail, so the bound is the clean-data figure less the outlier loss)."""
     require_gpu()
-    say(f"mx9 full size weights [4096, 14336] {dtype}: sampled parity, SNR")
+    say(f"mx9 full size weights [4096, 14336] {dtype}: SNR")
     x = synth.mx9_weights(4096, 14336, 4, dtype)
     xd = _to_dev(x)
     q, e, p = mxq.mx9_pack(xd)
     y = mxq.mx9_unpack(q, e, p, 4096, 14336, out_dtype=torch.float32 if dtype == "fp32" else torch.bfloat16)
-    torch.cuda.synchronize()
-    rows = sample_rows(4096, 64, 4)
-    nbr = 14336 // 16
-    sel = (rows[:, None] * nbr + np.arange(nbr)[None, :]).reshape(-1)
-    wq, we, wp = oracle.mx9_pack(np.ascontiguousarray(x[rows]), threads=THREADS)
-    hq, he, hp = host(q), host(e), host(p)
-    assert np.array_equal(hq[sel], wq) and np.array_equal(he[sel], we) and np.array_equal(hp[sel], wp)
-    wy = oracle.mx9_unpack(wq, we, wp, len(rows), 14336, dtype, threads=THREADS)
-    hy = host(y)[rows]
-    assert np.array_equal(hy.view(np.uint32 if dtype == "fp32" else np.uint16),
-                          wy.view(np.uint32 if dtype == "fp32" else np.uint16))
-    # whole-matrix properties: range of the exponent byte and round-trip quality
     assert int(e.min()) >= 1 and int(e.max()) <= 254 and int(q.abs().max()) <= 127
     xf = xd.float()
     snr = 10 * torch.log10((xf * xf).sum() / ((xf - y.float()) ** 2).sum()).item()
     say(f"  SNR {dtype}: {snr:.2f} dB")
     assert snr > 40.0
-
-
-def test_full_size_stress_sampled():
-    require_gpu()
-    say("mx9 full size stress bf16 [32768, 8192]: sampled parity")
-    x = synth.stress()
-    xd = _to_dev(x)
-    q, e, p = mxq.mx9_pack(xd)
-    y = mxq.mx9_unpack(q, e, p, 32768, 8192, out_dtype=torch.bfloat16)
-    torch.cuda.synchronize()
-    special = np.unique(np.argwhere((x & 0x7F80) == 0x7F80)[:, 0])
-    rows = np.unique(np.concatenate([sample_rows(32768, 48, 5), special[:64]]))
-    nbr = 8192 // 16
-    sel = (rows[:, None] * nbr + np.arange(nbr)[None, :]).reshape(-1)
-    wq, we, wp = oracle.mx9_pack(np.ascontiguousarray(x[rows]), threads=THREADS)
-    hq, he, hp = host(q), host(e), host(p)
-    assert np.array_equal(hq[sel], wq) and np.array_equal(he[sel], we) and np.array_equal(hp[sel], wp)
-    wy = oracle.mx9_unpack(wq, we, wp, len(rows), 8192, "bf16", threads=THREADS)
-    assert np.array_equal(host(y)[rows], wy)
-    assert int((e == 255).sum()) >= 1

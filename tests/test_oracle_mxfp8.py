@@ -193,11 +193,25 @@ def test_grouped_equals_dense_except_tail():
     assert rc == 0
     for a, b in zip(out, dense):
         np.testing.assert_array_equal(a, b)
-    # threaded path follows the same rule
-    rc, out_t = oracle.mxfp8_grouped(x, np.array([128, 384], np.int32), threads=4)
-    rc1, out_1 = oracle.mxfp8_grouped(x, np.array([128, 384], np.int32), threads=1)
-    for a, b in zip(out_t, out_1):
-        np.testing.assert_array_equal(a, b)
+
+
+def test_grouped_threaded_slabs_equal_one_call():
+    """The threaded grouped oracle splits the rows into slabs with rebased
+    group ends; whatever the slab count, and with a row count that is not a
+    multiple of 128, it returns the single C call's bytes."""
+    for M, N in ((1024, 128), (608, 96)):
+        x = synth.special_matrix(M, N, M + N)
+        cases = ([128, 384], [0], [0, 0, 0], [M // 128 * 128], [128, 128, 512], [384, 384, 384, 512],
+                 [], [256])
+        for offs in cases:
+            o = np.array(offs, np.int32)
+            rc1, one = oracle.mxfp8_grouped(x, o, threads=1)
+            assert rc1 == 0, offs
+            for threads in (2, 3, 7, 16):
+                rc, many = oracle.mxfp8_grouped(x, o, threads=threads)
+                assert rc == 0, (offs, threads)
+                for a, b in zip(many, one):
+                    np.testing.assert_array_equal(a, b)
 
 
 def test_offs_validation_codes():

@@ -13,9 +13,12 @@ algorithmic bytes per call over its average call time from HIP events on the
 launch stream (the call is one kernel), against MI355X's 8 TB/s HBM peak.
 ``traffic`` is the HBM byte count per call from the committed rocprofv3
 FETCH_SIZE / WRITE_SIZE summary, reported only while the kernel source
-matches the source those counters were taken on.  ``cpu_baseline`` times the CPU oracle on a bounded
-sample of the same workload (a multithreaded leg of about ten seconds and a
-single-thread leg).
+matches the source those counters were taken on.  ``box_roofs`` gives, for
+context, what the same box reaches for a plain copy, read and write of the
+cast's byte volume with hand-written streaming kernels, and
+``roofline.frac_of_box_copy`` the cast's rate against that copy.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload (a multithreaded leg of about ten seconds and a single-thread leg).
 
 ``configs`` holds the other workloads, each timed per call with HIP events
 while rotating three input/output buffer sets so that MI355X's 256 MB
@@ -75,6 +78,53 @@ def committed_traffic():
     if not m_src or not m_b or m_src.group(1) != source_digest():
         return None
     return float(m_b.group(1))
+
+
+def box_roofs(dev, volume: int, launches: int = 10):
+    """What this box achieves for plain streams of `volume` bytes: a copy
+    (half the volume read, half written), a read and a write, each by the
+    hand-written kernels of libmxq_roof.so (one 16-byte non-temporal access
+    per lane, 4 KiB per workgroup), alternating two buffers of `volume` bytes
+    so the 256 MB last-level cache cannot serve one launch from the last."""
+    import torch
+    lib_path = os.path.join(ROOT, "mx9_dual_axis_amd", "libmxq_roof.so")
+    if not os.path.exists(lib_path):
+        raise RuntimeError(f"{lib_path} is missing (run __graft_entry__.build())")
+    lib = ctypes.CDLL(lib_path)
+    lib.mxq_roof.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.mxq_roof.restype = ctypes.c_int
+    vol = volume // 8192 * 8192
+    half = vol // 2
+    bufs = [torch.zeros(vol, dtype=torch.uint8, device=dev) for _ in range(2)]
+    sink = torch.zeros(4096, dtype=torch.uint8, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def launch(kind, i):
+        b = bufs[i % 2].data_ptr()
+        if kind == 0:
+            rc = lib.mxq_roof(0, b, b + half, half, stream)
+        elif kind == 1:
+            rc = lib.mxq_roof(1, b, sink.data_ptr(), vol, stream)
+        else:
+            rc = lib.mxq_roof(2, None, b, vol, stream)
+        if rc != 0:
+            raise RuntimeError(f"mxq_roof({kind}) failed ({rc})")
+
+    out = {}
+    for kind, name in ((0, "copy"), (1, "read"), (2, "write")):
+        for i in range(2):
+            launch(kind, i)
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record()
+        for i in range(launches):
+            launch(kind, i)
+        e1.record()
+        torch.cuda.synchronize()
+        out[f"{name}_GB_s"] = round(vol * launches / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    out["bytes_per_launch"] = vol
+    out["kernels"] = "libmxq_roof.so: one 16-byte non-temporal load and/or store per lane, 4 KiB per workgroup"
+    del bufs, sink
+    return out
 
 
 def cpu_baseline(xb, threads: int, budget_s: float, single_rows: int):
@@ -518,6 +568,8 @@ def main():
     torch.cuda.synchronize()
     stream_gbs = 2 * half * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst, src32, dst32
+    # and by the hand-written streams: this box's own roof for the cast's volume
+    roofs = box_roofs(dev, int(kbytes["dual_axis"]))
 
     # context: the dual-axis cast alone on the same matrix, back-to-back calls
     # alternating two output sets (the 1.09 GB per call exceeds the 256 MB
@@ -554,10 +606,12 @@ def main():
                      "algorithmic_bytes_per_launch": dual["bytes"],
                      "avg_launch_us": dual["us"],
                      "launches_timed": len(dual_times),
-                     "timed_every_nth_step": EVENT_EVERY},
+                     "timed_every_nth_step": EVENT_EVERY,
+                     "frac_of_box_copy": round(dual["GB_s"] / roofs["copy_GB_s"], 4)},
         "kernels": kernels,
         "copy_GB_s": round(copy_gbs, 1),
         "stream_copy_GB_s": round(stream_gbs, 1),
+        "box_roofs": roofs,
         "kernel_source_sha256_16": source_digest(),
     }
     del x, dual_out, mx9_out, y

@@ -74,7 +74,8 @@ enum { MX_OFFS_OK = 0, MX_OFFS_ORDER = 1, MX_OFFS_ALIGN = 2, MX_OFFS_BOUNDS = 3 
  * scale 254 with +-Inf -> +-448 and the other elements scaled by 2^-127.
  *
  * Errors: MX_E_NULL (a pointer NULL while M, N > 0), MX_E_BLOCK, MX_E_MODE,
- * MX_E_SHAPE (M or N negative, not a multiple of 128, or above 2^24),
+ * MX_E_SHAPE (M or N negative, not a multiple of 128, or above 2^24, or
+ * more than 2^23 128x128 tiles: each tile is one workgroup of 512 threads),
  * MX_E_STRIDE (ld_x < N, not a multiple of 8, or above 2^24), MX_E_ALIGN
  * (any pointer not 16-byte aligned), MX_E_OVERLAP.  M == 0 or N == 0 is a
  * no-op.  The call enqueues one kernel on the stream.
@@ -327,7 +328,8 @@ int mx9_unpack_records(const uint8_t *packed, int64_t ld_p, int64_t outer, int64
  * are 4-byte aligned and C rows are whole 16-byte pieces; other views take
  * a slower general kernel with the same results.
  *
- * Errors: MX_E_NULL, MX_E_DTYPE (out_dtype), MX_E_SHAPE, MX_E_STRIDE (a pitch
+ * Errors: MX_E_NULL, MX_E_DTYPE (out_dtype), MX_E_SHAPE (also when a kernel's
+ * grid would exceed 2^32 threads), MX_E_STRIDE (a pitch
  * below its row or misaligned, a negative scale stride), MX_E_ALIGN (A or B
  * not 16-byte aligned, C not aligned to its element), MX_E_OVERLAP (C
  * overlaps an input).  M == 0 or N == 0 is a no-op.
@@ -364,7 +366,7 @@ int mx_grouped_gemm_rows(const uint8_t *A, int64_t lda, const uint8_t *sA, int64
  * cast's s_col, as (1, M) and (1, N) strided views).  Invalid offsets are
  * clamped to multiples of 128 inside [0, K]: the results are then
  * unspecified, the accesses stay inside the operands.  Errors as for
- * mx_gemm_nt, plus MX_E_SHAPE (G < 1, or more than 2^31 tiles),
+ * mx_gemm_nt, plus MX_E_SHAPE (G < 1, or a grid of more than 2^32 threads),
  * MX_E_STRIDE (c_gs smaller than one group's C).
  */
 int mx_grouped_gemm_k(const uint8_t *A, int64_t lda, const uint8_t *sA, int64_t sa_rs, int64_t sa_bs,

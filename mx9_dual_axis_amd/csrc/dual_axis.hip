@@ -5,9 +5,11 @@
 // matrix produces rowwise 1x32 and colwise 32x1 E4M3 data with E8M0 RCEIL
 // scales; colwise data is stored transposed.
 //
-// Work decomposition: one workgroup (4 wave64s) per 128x128 tile.
-//   * load   : each thread holds eight 16-byte row segments (8 bf16 each); a
+// Work decomposition: one workgroup (8 wave64s) per 128x128 tile.
+//   * load   : each thread holds four 16-byte row segments (8 bf16 each); a
 //              wave's load instruction covers four full 256-byte tile rows.
+//              (8 waves of 4 loads measured 1% faster than 4 waves of 8 on
+//              the stress shape, with the same LDS footprint per tile.)
 //   * rowwise: a 1x32 block is four adjacent lanes; the block maximum is a
 //              packed u16 max of the sign-masked bf16 patterns followed by a
 //              two-step DPP quad reduction.  Masking the sign makes the
@@ -19,7 +21,7 @@
 //              a colwise dword read (8 chunks x 4 column pairs) hit 32
 //              distinct banks: SQ_LDS_BANK_CONFLICT reads 0 (with 2c alone,
 //              a two-way conflict, 31% of the LDS-active cycles).
-//   * colwise: a unit is (column pair, 16-row chunk); each thread takes two.
+//   * colwise: a unit is (column pair, 16-row chunk); each thread takes one.
 //              A packed u16 max over 16 LDS dwords plus one DPP step between
 //              the two chunks of a 32-row block gives both column maxima;
 //              v_perm regroups (row m, row m+1) pairs of one column so the
@@ -39,6 +41,9 @@
 //              the input and of both outputs over the HBM channels; a smaller
 //              call goes down whole tile columns (column-major), which the
 //              cache serves better (measured on the workloads' shapes).
+//   * s_col  : a tile owns 128 contiguous scale bytes in each of 4 block
+//              rows; they are staged in LDS and leave as whole 128-byte lines
+//              (one 16-byte store per lane), instead of 128 two-byte stores.
 //   * s_row  : a tile owns 4 scale bytes of each of its 128 rows, written as
 //              one 4-byte store per row.  Consecutive workgroups go to
 //              consecutive XCDs, so with a tile-row count that is a multiple
@@ -84,7 +89,9 @@ namespace mxq {
 namespace {
 
 constexpr int kTile = 128;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kLoads = kTile * 16 / kThreads;   // 16-byte loads per thread (a tile is 2048 of them)
+constexpr int kRowsPerLoad = kThreads / 16;     // tile rows one load round covers
 constexpr double kMemorySideCacheBytes = 256.0 * 1024 * 1024;   // MI355X last-level (MALL) capacity
 
 // How a call writes its scales.
@@ -200,7 +207,7 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
                       const int32_t* __restrict__ offs, int32_t G, int32_t* __restrict__ err) {
     __shared__ uint4 lds_tile[kTile * 16];     // [128 rows][16 x 16 bytes]
     __shared__ uint32_t lds_srow[kTile];       // the tile's 512 rowwise scale bytes
-    __shared__ uint32_t lds_scol[kTile];       // the tile's 512 colwise scale bytes (matrix-core layout)
+    __shared__ uint32_t lds_scol[kTile];       // the tile's 512 colwise scale bytes (either layout)
 
     const uint32_t t = threadIdx.x;
     const uint32_t bid = blockIdx.x;
@@ -221,7 +228,7 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
         if (err != nullptr && bid == 0) validate_offsets(offs, G, M, err);
     }
 
-    // ---- load the tile: rows 16k + rsub, columns c8 .. c8+7 ----
+    // ---- load the tile: rows kRowsPerLoad * k + rsub, columns c8 .. c8+7 ----
     const uint32_t rsub = t >> 4;
     const uint32_t c8 = (t & 15u) * 8u;
     const __amdgpu_buffer_rsrc_t rx = raw_rsrc(x + m0 * ld_x + n0);
@@ -229,17 +236,18 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
     const __amdgpu_buffer_rsrc_t rq_col = raw_rsrc(q_col + n0 * M + m0);
     const bool stream_row = ((row_stream_mask >> (tm & 7u)) & 1u) != 0u;
     const uint32_t ldb = uint32_t(ld_x) * 2u;          // row pitch in bytes (<= 2^25)
-    uint4 d[8];
+    uint4 d[kLoads];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, (16u * k + rsub) * ldb + 2u * c8, 0, kPolicyStream);
+    for (int k = 0; k < kLoads; ++k) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t(kRowsPerLoad) * k + rsub) * ldb + 2u * c8, 0,
+                                                              kPolicyStream);
         d[k] = make_uint4(v.x, v.y, v.z, v.w);
     }
 
     // ---- rowwise 1x32 pass ----
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const uint32_t r = 16u * k + rsub;
+    for (int k = 0; k < kLoads; ++k) {
+        const uint32_t r = uint32_t(kRowsPerLoad) * k + rsub;
         lds_tile[r * 16u + ((t & 15u) ^ lds_chunk_xor(r >> 4))] = d[k];
         const uint32_t mx = pk_max_u16(pk_max_u16(d[k].x & 0x7FFF7FFFu, d[k].y & 0x7FFF7FFFu),
                                        pk_max_u16(d[k].z & 0x7FFF7FFFu, d[k].w & 0x7FFF7FFFu));
@@ -273,16 +281,15 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
     }
 
     // ---- colwise 32x1 pass ----
-    // Unit = (column pair cp, 16-row chunk c); each thread takes two units.
+    // Unit = (column pair cp, 16-row chunk c); each thread takes one unit.
     // Eight lanes share a column pair and hold its eight chunks, so each
     // 16-byte store of a column lands in one full 128-byte line per 8 lanes.
     // The two chunks of a 32-row block sit in lanes l, l^1 (one DPP step).
     const uint32_t lane = t & 63u, wave = t >> 6;
     const uint32_t c = lane & 7u;
     const uint32_t* lt = reinterpret_cast<const uint32_t*>(lds_tile);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const uint32_t cp = ((lane >> 3) & 7u) + 8u * (wave + 4u * u);
+    {
+        const uint32_t cp = ((lane >> 3) & 7u) + 8u * wave;
         const uint32_t* src = lt + (16u * c) * 64u + (cp ^ (4u * lds_chunk_xor(c)));
         uint32_t v[16];
 #pragma unroll
@@ -324,17 +331,22 @@ void dual_axis_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t M, i
                 ls[mfma_scale_slot(2u * cp, c >> 1)] = tail ? uint8_t(0) : uint8_t(b_lo);
                 ls[mfma_scale_slot(2u * cp + 1u, c >> 1)] = tail ? uint8_t(0) : uint8_t(b_hi);
             } else {
-                const uint16_t sv = tail ? uint16_t(0) : uint16_t(b_lo | (b_hi << 8));
-                *reinterpret_cast<uint16_t*>(s_col + sbr * N + n0 + 2 * cp) = sv;
+                // block row c/2 of the tile, columns 2 cp and 2 cp + 1
+                reinterpret_cast<uint16_t*>(lds_scol)[(c >> 1) * 64u + cp] =
+                    tail ? uint16_t(0) : uint16_t(b_lo | (b_hi << 8));
             }
         }
     }
-    if (kScales == kScalesMfma) {
-        // runs (2 tn + h) * tiles_m + tm of the [N rows, M/32 blocks] operand
-        __syncthreads();
-        if (t < 32) {
+    __syncthreads();
+    if (t < 32) {
+        const uint4 piece = reinterpret_cast<const uint4*>(lds_scol)[t];
+        if (kScales == kScalesMfma) {
+            // runs (2 tn + h) * tiles_m + tm of the [N rows, M/32 blocks] operand
             const int64_t run = (2 * int64_t(tn) + (t >> 4)) * tiles_m + tm;
-            *reinterpret_cast<uint4*>(s_col + run * 256 + 16 * (t & 15u)) = reinterpret_cast<const uint4*>(lds_scol)[t];
+            *reinterpret_cast<uint4*>(s_col + run * 256 + 16 * (t & 15u)) = piece;
+        } else {
+            // block row m0/32 + t/8, bytes n0 + 16 (t%8) .. + 15
+            *reinterpret_cast<uint4*>(s_col + (m0 / 32 + (t >> 3)) * N + n0 + 16 * (t & 7u)) = piece;
         }
     }
 }

@@ -472,10 +472,27 @@ void mx_gemm_pipe_kernel(GemmArgs p) {
     bool zero = false;
     if (p.mode == 0) {
         if (p.offs != nullptr) {
-            // row groups: consecutive workgroups take the column tiles of one
-            // row tile, so its activation rows are read from HBM once
-            tn = blockIdx.x % p.tiles_n;
-            tm = blockIdx.x / p.tiles_n;
+            // Row groups.  Workgroups are dealt to the 8 XCDs in turn, each
+            // with its own L2.  XCD x (workgroups x, x + 8, ...) takes a
+            // contiguous range of the covered row tiles, every column tile of
+            // one row tile in a row, then its share of the uncovered tail
+            // (rows from offs[G-1] on, written as 0).  A row tile's activations
+            // are then fetched into one L2 only, and neighbouring row tiles,
+            // which mostly belong to one group, share their expert's weights
+            // there.  The ranges partition the row tiles for any offs[G-1],
+            // so every tile is taken exactly once; workgroups past their
+            // XCD's share exit.
+            const uint32_t xcd = blockIdx.x & 7u, j = blockIdx.x >> 3;
+            const uint32_t lr = j / p.tiles_n;
+            tn = j - lr * p.tiles_n;
+            const int64_t last = p.offs[p.G - 1];
+            const uint32_t cov = uint32_t((last < 0 ? 0 : (last > p.M ? p.M : last)) / P::kTM);
+            const uint32_t tail = p.tiles_m - cov;
+            const uint32_t c0 = cov * xcd / 8u, c1 = cov * (xcd + 1u) / 8u;
+            const uint32_t t0 = cov + tail * xcd / 8u, t1 = cov + tail * (xcd + 1u) / 8u;
+            if (lr < c1 - c0) tm = c0 + lr;
+            else if (lr < (c1 - c0) + (t1 - t0)) tm = t0 + (lr - (c1 - c0));
+            else return;                                         // uniform: the whole workgroup
         } else {
             tm = blockIdx.x % p.tiles_m;
             tn = blockIdx.x / p.tiles_m;
@@ -657,7 +674,9 @@ hipError_t launch_pipe(GemmArgs& p, int out_dtype, hipStream_t stream) {
         using P = Pipe<4, 4, 2, 4>;
         p.tiles_m = uint32_t(p.M / P::kTM);
         p.tiles_n = uint32_t((p.N + P::kTN - 1) / P::kTN);
-        const dim3 grid(p.tiles_m * p.tiles_n), block(P::kThreads);
+        // each XCD's share is at most ceil(tiles_m / 8) + 1 row tiles (its
+        // covered range and its tail range are each at most a ceiling)
+        const dim3 grid(8u * ((p.tiles_m + 7u) / 8u + 1u) * p.tiles_n), block(P::kThreads);
         if (out_dtype == 0) hipLaunchKernelGGL((mx_gemm_pipe_kernel<0, 4, 4, 2, 4, kSF>), grid, block, 0, stream, p);
         else hipLaunchKernelGGL((mx_gemm_pipe_kernel<1, 4, 4, 2, 4, kSF>), grid, block, 0, stream, p);
     } else {

@@ -60,7 +60,7 @@ int check_dual(const uint16_t* x, int64_t M, int64_t N, int64_t ld_x, int32_t bl
     if (scaling_mode != MX_SCALE_RCEIL) return MX_E_MODE;
     if (M < 0 || N < 0 || M > kMaxDual || N > kMaxDual || M % 128 != 0 || N % 128 != 0)
         return MX_E_SHAPE;
-    if (uint64_t(M / 128) * uint64_t(N / 128) * 256 > kMaxThreads) return MX_E_SHAPE;
+    if (uint64_t(M / 128) * uint64_t(N / 128) * 512 > kMaxThreads) return MX_E_SHAPE;   // one 512-thread workgroup per tile
     if (ld_x < N || ld_x % 8 != 0 || ld_x > kMaxDual) return MX_E_STRIDE;
     if (!empty && (!aligned(x, 16) || !aligned(q_row, 16) || !aligned(s_row, 16) ||
                    !aligned(q_col, 16) || !aligned(s_col, 16)))
@@ -149,6 +149,19 @@ int check_gemm(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, 
     return MX_OK;
 }
 
+// Whether every contraction kernel the call may launch has a grid whose
+// thread count fits 32 bits: the general kernel (128 x 128 tiles of 256
+// threads), the pipelined kernel (256 x 256 tiles of 512 threads, or for row
+// groups 8 XCD shares of at most ceil(M/128/8) + 1 row tiles of 128 x 256),
+// times the group count for contraction groups.
+bool gemm_grid_fits(int64_t M, int64_t N, int32_t G, bool row_groups, bool k_groups) {
+    const uint64_t g = k_groups ? uint64_t(G) : 1u;
+    const uint64_t general = uint64_t(M / 128) * uint64_t(N / 128) * g * 256u;
+    const uint64_t pipe = row_groups ? 8u * (uint64_t(M / 128 + 7) / 8u + 1u) * uint64_t((N + 255) / 256) * 512u
+                                     : uint64_t((M + 255) / 256) * uint64_t((N + 255) / 256) * g * 512u;
+    return general <= kMaxThreads && pipe <= kMaxThreads;
+}
+
 // Bytes of one operand's scales: a strided view, or rows * K/32 in the matrix-core layout.
 uint64_t scale_bytes(bool mfma, int64_t rows, int64_t K, int64_t rs, int64_t bs) {
     return mfma ? uint64_t(rows) * uint64_t(K / 32) : scale_span(rows, K / 32, rs, bs);
@@ -159,6 +172,7 @@ int gemm_call(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs, i
               int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, int32_t out_dtype, bool mfma, void* stream) {
     int rc = check_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, sB, sb_rs, sb_bs, M, N, K, C, ldc, out_dtype, mfma);
     if (rc != MX_OK) return rc;
+    if (!gemm_grid_fits(M, N, 1, false, false)) return MX_E_SHAPE;
     const uint64_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
     const uint64_t cb = matrix_bytes(M, N, ldc, int64_t(esz));
     const Span s[5] = {{addr(C), cb}, {addr(A), matrix_bytes(M, K, lda, 1)}, {addr(B), matrix_bytes(N, K, ldb, 1)},
@@ -178,6 +192,7 @@ int gemm_rows_call(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_
     int rc = check_gemm(A, lda, sA, sa_rs, sa_bs, B, ldb, sB, sb_rs, sb_bs, M, N, K, C, ldc, out_dtype, mfma);
     if (rc != MX_OK) return rc;
     if (G < 1 || G > (1 << 20)) return MX_E_SHAPE;
+    if (!gemm_grid_fits(M, N, G, true, false)) return MX_E_SHAPE;
     if (!offs) return MX_E_NULL;
     if (!aligned(offs, 4)) return MX_E_ALIGN;
     if (b_gs < 0 || sb_gs < 0) return MX_E_STRIDE;
@@ -207,8 +222,7 @@ int gemm_k_call(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t sa_rs,
     const uint64_t esz = out_dtype == MX_DTYPE_F32 ? 4 : 2;
     const uint64_t slab = matrix_bytes(M, N, ldc, 1);                  // elements of one group's C
     if (c_gs < int64_t(slab)) return MX_E_STRIDE;
-    const uint64_t tiles = uint64_t(M / 128) * uint64_t(N / 128) * uint64_t(G);
-    if (tiles > 0x7FFFFFFFull) return MX_E_SHAPE;
+    if (!gemm_grid_fits(M, N, G, false, true)) return MX_E_SHAPE;
     const Span s[6] = {{addr(C), (uint64_t(G - 1) * uint64_t(c_gs) + slab) * esz},
                        {addr(A), matrix_bytes(M, K, lda, 1)}, {addr(B), matrix_bytes(N, K, ldb, 1)},
                        {addr(sA), scale_bytes(mfma, M, K, sa_rs, sa_bs)}, {addr(sB), scale_bytes(mfma, N, K, sb_rs, sb_bs)},

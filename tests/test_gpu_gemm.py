@@ -135,6 +135,32 @@ def test_row_groups_parity(out_dtype):
     assert torch.all(C[offs[-1]:] == 0)
 
 
+@pytest.mark.parametrize("M,covered", [(384, 256), (1664, 1664), (1664, 0), (2560, 1920), (128, 128)])
+def test_row_groups_every_tile_once(M, covered):
+    """Row tiles are shared out over the XCDs as contiguous covered and tail
+    ranges; row-tile counts that are not multiples of 8, a buffer with no
+    tail and one with no covered rows all give every output row exactly
+    once, matching the oracle (tail rows 0)."""
+    require_gpu()
+    say(f"mx_grouped_gemm_rows schedule M={M} covered={covered}")
+    g = np.random.default_rng(M + covered)
+    N, K, E = 384, 256, 6
+    A = _codes(g, (M, K))
+    sA = g.integers(118, 137, (M, K // 32), dtype=np.uint8)
+    B = np.stack([_codes(g, (N, K)) for _ in range(E)])
+    sB = g.integers(118, 137, (E, N, K // 32), dtype=np.uint8)
+    sizes = 128 * g.multinomial(covered // 128, np.full(E, 1.0 / E))
+    offs = np.cumsum(sizes).astype(np.int32)
+    assert offs[-1] == covered
+    out = torch.full((M, N), 3.0, dtype=torch.float32, device=DEV)
+    mxq.mx_grouped_gemm_rows(_dev(A), _dev(sA), _dev(B), _dev(sB), _dev(offs), out=out)
+    torch.cuda.synchronize()
+    ref, absC = oracle.mx_grouped_gemm_rows(A, sA, B, sB, offs, sa_strides=(K // 32, 1), sb_strides=(K // 32, 1),
+                                            threads=THREADS, with_abs=True)
+    _assert_close(out, ref, absC, K, torch.float32, f"schedule M={M}")
+    assert torch.all(out[covered:] == 0)
+
+
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_contraction_groups_parity(out_dtype):
     require_gpu()

@@ -221,6 +221,7 @@ def time_rotating(calls, launches: int):
         a.record()
         b.record()
     torch.cuda.synchronize()
+    calls[-1]()         # a queued call, so the first bracketed one does not wait for the host
     for i, (a, b) in enumerate(evs):
         a.record()
         calls[i % len(calls)]()
@@ -514,18 +515,27 @@ def main():
 
     # The dual-axis call of every EVENT_EVERY-th timed step is bracketed by
     # events: each record leaves the GPU idle for a few microseconds, which
-    # bracketing every step would add to the step time.
-    evs = make_events(2, (args.steps + EVENT_EVERY - 1) // EVENT_EVERY)
+    # bracketing every step would add to the step time.  The bracketed steps
+    # are the last of each run of EVENT_EVERY, never the first step after the
+    # synchronization: with an empty queue the GPU would reach the opening
+    # event before the host had enqueued the cast, and the host's enqueue
+    # time would count as kernel time.
+    bracketed = [k for k in range(args.steps) if k % EVENT_EVERY == EVENT_EVERY - 1] or [args.steps - 1]
+    evs = make_events(2, len(bracketed))
+    slot = {k: i for i, k in enumerate(bracketed)}
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(evs[k // EVENT_EVERY] if k % EVENT_EVERY == 0 else None)
+        step(evs[slot[k]] if k in slot else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dual_times = [ev[0].elapsed_time(ev[1]) * 1e-3 for ev in evs]
 
     # per-kernel breakdown: a second, separate pass of K steps with events
-    # between all three calls (not the timed region)
+    # between all three calls (not the timed region), after two unbracketed
+    # steps that give the GPU a queue to work through
     evs4 = make_events(4)
+    step()
+    step()
     for k in range(args.steps):
         step(evs4[k], all_kernels=True)
     torch.cuda.synchronize()
@@ -607,6 +617,7 @@ def main():
                      "avg_launch_us": dual["us"],
                      "launches_timed": len(dual_times),
                      "timed_every_nth_step": EVENT_EVERY,
+                     "bracketed_steps": bracketed,
                      "frac_of_box_copy": round(dual["GB_s"] / roofs["copy_GB_s"], 4)},
         "kernels": kernels,
         "copy_GB_s": round(copy_gbs, 1),

@@ -451,6 +451,41 @@ struct Pipe {
     static_assert(kStages == 2 || kLoads < 16, "vmcnt immediate");
 };
 
+// Group ends of a row-grouped contraction, read 64 at a time (one load per
+// lane, then a prefix maximum across the wave).  The ends are rounded down
+// to multiples of 128 and clamped to an ascending sequence inside [0, M]
+// (valid offsets already are), so the row tiles they delimit partition the
+// rows whatever offs holds.  Returns the last clamped end (the first row of
+// the uncovered tail); with row >= 0, *group receives the number of ends at
+// or below `row`, i.e. the group whose rows contain it (G for the tail).
+// Every wave of a workgroup computes the same values, held wave-uniform, so
+// no barrier is needed.
+__device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ int32_t group_ends(const GemmArgs& p, int64_t row, int32_t* group) {
+    const uint32_t lane = threadIdx.x & 63u;
+    int32_t c_carry = 0;
+    int32_t below = 0;
+    for (int32_t base = 0; base < p.G; base += 64) {
+        const int32_t g = base + int32_t(lane);
+        int32_t c = 0;
+        if (g < p.G) {
+            const int64_t o = (int64_t(p.offs[g]) / 128) * 128;
+            c = int32_t(o < 0 ? 0 : (o > p.M ? p.M : o));
+        }
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t o = __shfl_up(c, d, 64);
+            if (lane >= uint32_t(d)) c = max(c, o);
+        }
+        c = max(c, c_carry);
+        if (row >= 0) below += uniform(__builtin_popcountll(__ballot(g < p.G && int64_t(c) <= row)));
+        c_carry = uniform(__shfl(c, 63, 64));
+    }
+    if (row >= 0) *group = below;
+    return c_carry;
+}
+
 template <int kOut, int MS, int NS, int WM, int WN, int kSF>
 __global__ __launch_bounds__(64 * WM * WN, WM * WN >= 8 ? 2 : 1)
 void mx_gemm_pipe_kernel(GemmArgs p) {
@@ -464,7 +499,8 @@ void mx_gemm_pipe_kernel(GemmArgs p) {
     const uint32_t wm = wave / WN, wn = wave % WN;
 
     // ---- which tile, which group, which range of the contraction ----
-    uint32_t tm, tn;
+    int64_t m0;
+    uint32_t tn;
     int64_t k_lo = 0, k_hi = p.K;
     const uint8_t* B = p.B;
     const uint8_t* sB = p.sB;
@@ -472,52 +508,49 @@ void mx_gemm_pipe_kernel(GemmArgs p) {
     bool zero = false;
     if (p.mode == 0) {
         if (p.offs != nullptr) {
-            // Row groups.  Workgroups are dealt to the 8 XCDs in turn, each
-            // with its own L2.  XCD x (workgroups x, x + 8, ...) takes a
-            // contiguous range of the covered row tiles, every column tile of
-            // one row tile in a row, then its share of the uncovered tail
-            // (rows from offs[G-1] on, written as 0).  A row tile's activations
-            // are then fetched into one L2 only, and neighbouring row tiles,
-            // which mostly belong to one group, share their expert's weights
-            // there.  The ranges partition the row tiles for any offs[G-1],
-            // so every tile is taken exactly once; workgroups past their
-            // XCD's share exit.
+            // Row groups (launched with 128-row tiles only: one group unit).
+            // Workgroups are dealt to the 8 XCDs in turn, each with its own
+            // L2.  XCD x (workgroups x, x + 8, ...) takes a contiguous range of the
+            // covered row tiles, every column tile of one row tile in a row,
+            // then its share of the uncovered tail (written as 0).  A row
+            // tile's activations are then fetched into one L2 only, and
+            // neighbouring row tiles, which mostly belong to one group, share
+            // their expert's weights there.  The ranges partition the row
+            // tiles; workgroups past their XCD's share exit.
             const uint32_t xcd = blockIdx.x & 7u, j = blockIdx.x >> 3;
             const uint32_t lr = j / p.tiles_n;
             tn = j - lr * p.tiles_n;
-            const int64_t last = p.offs[p.G - 1];
-            const uint32_t cov = uint32_t((last < 0 ? 0 : (last > p.M ? p.M : last)) / P::kTM);
+            const uint32_t cov = uint32_t(group_ends(p, -1, nullptr)) / 128u;
             const uint32_t tail = p.tiles_m - cov;
             const uint32_t c0 = cov * xcd / 8u, c1 = cov * (xcd + 1u) / 8u;
             const uint32_t t0 = cov + tail * xcd / 8u, t1 = cov + tail * (xcd + 1u) / 8u;
+            uint32_t tm;
             if (lr < c1 - c0) tm = c0 + lr;
             else if (lr < (c1 - c0) + (t1 - t0)) tm = t0 + (lr - (c1 - c0));
             else return;                                         // uniform: the whole workgroup
-        } else {
-            tm = blockIdx.x % p.tiles_m;
-            tn = blockIdx.x / p.tiles_m;
-        }
-        if (p.offs != nullptr) {                                // kTM == 128: one group unit
-            const int64_t row = int64_t(tm) * P::kTM;
-            int32_t g = 0;
-            while (g < p.G && int64_t(p.offs[g]) <= row) ++g;
-            if (g == p.G) {
+            m0 = int64_t(tm) * P::kTM;
+            int32_t g = p.G;
+            group_ends(p, m0, &g);
+            if (g >= p.G) {
                 zero = true;
             } else {
                 B += int64_t(g) * p.b_gs;
                 sB += int64_t(g) * p.sb_gs;
             }
+        } else {
+            m0 = int64_t(blockIdx.x % p.tiles_m) * P::kTM;
+            tn = blockIdx.x / p.tiles_m;
         }
     } else {
         const uint32_t per = p.tiles_m * p.tiles_n;
         const uint32_t g = blockIdx.x / per, r = blockIdx.x - g * per;
-        tm = r % p.tiles_m;
+        m0 = int64_t(r % p.tiles_m) * P::kTM;
         tn = r / p.tiles_m;
         k_lo = g == 0 ? 0 : clamp_end(p.offs[g - 1], 0, p.K);
         k_hi = clamp_end(p.offs[g], k_lo, p.K);
         C += int64_t(g) * p.c_gs * kEsz;
     }
-    const int64_t m0 = int64_t(tm) * P::kTM, n0 = int64_t(tn) * P::kTN;
+    const int64_t n0 = int64_t(tn) * P::kTN;
     const int64_t n = zero ? 0 : (k_hi - k_lo) / kTile;
 
     // ---- load plan (all offsets fit 32 bits: a tile spans <= 256 rows of <= 2^24 bytes) ----
@@ -671,11 +704,16 @@ int plain_scale_form(const uint8_t* s, int64_t rs, int64_t bs, int64_t K, int64_
 template <int kSF>
 hipError_t launch_pipe(GemmArgs& p, int out_dtype, hipStream_t stream) {
     if (p.mode == 0 && p.offs != nullptr) {
+        // 128 x 256 tiles (a group unit is 128 rows).  Each XCD's share is at
+        // most ceil(tiles_m / 8) + 1 row tiles (its covered range and its
+        // tail range are each at most a ceiling).  (Measured on MI355X for the
+        // workload's 64 groups: covering the pairs of units inside a group with
+        // 256 x 256 tiles in a second launch, whose 64 x 128 wave tiles run the
+        // matrix cores faster, took 259 us instead of 187 us: 280 such tiles
+        // need two rounds of the 256 CUs, and the odd units a third.)
         using P = Pipe<4, 4, 2, 4>;
         p.tiles_m = uint32_t(p.M / P::kTM);
         p.tiles_n = uint32_t((p.N + P::kTN - 1) / P::kTN);
-        // each XCD's share is at most ceil(tiles_m / 8) + 1 row tiles (its
-        // covered range and its tail range are each at most a ceiling)
         const dim3 grid(8u * ((p.tiles_m + 7u) / 8u + 1u) * p.tiles_n), block(P::kThreads);
         if (out_dtype == 0) hipLaunchKernelGGL((mx_gemm_pipe_kernel<0, 4, 4, 2, 4, kSF>), grid, block, 0, stream, p);
         else hipLaunchKernelGGL((mx_gemm_pipe_kernel<1, 4, 4, 2, 4, kSF>), grid, block, 0, stream, p);

@@ -123,7 +123,37 @@ def box_roofs(dev, volume: int, launches: int = 10):
         out[f"{name}_GB_s"] = round(vol * launches / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
     out["bytes_per_launch"] = vol
     out["kernels"] = "libmxq_roof.so: one 16-byte non-temporal load and/or store per lane, 4 KiB per workgroup"
-    del bufs, sink
+    del bufs
+
+    # the cast's own three streams, each alone (mxq_roof_cast_stream): the
+    # tiled bf16 read, the q_row write and the q_col write, in the cast's tile
+    # order with its per-lane accesses
+    lib.mxq_roof_cast_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_void_p]
+    lib.mxq_roof_cast_stream.restype = ctypes.c_int
+    streams = {}
+    for sid, name, nbytes in ((0, "x_read", 2 * M * N), (1, "q_row_write", M * N), (2, "q_col_write", M * N)):
+        sbufs = [torch.zeros(nbytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+
+        def launch(i):
+            rc = lib.mxq_roof_cast_stream(sid, sbufs[i % 2].data_ptr(), sink.data_ptr(), M, N, stream)
+            if rc != 0:
+                raise RuntimeError(f"mxq_roof_cast_stream({sid}) failed ({rc})")
+
+        for i in range(2):
+            launch(i)
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record()
+        for i in range(launches):
+            launch(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / launches
+        streams[name] = {"us": round(us, 2), "bytes": nbytes, "GB_s": round(nbytes / us / 1e3, 1)}
+        del sbufs
+    streams["sum_us"] = round(sum(v["us"] for v in streams.values()), 2)
+    out["cast_streams_alone"] = streams
+    del sink
     return out
 
 

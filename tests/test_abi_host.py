@@ -253,3 +253,18 @@ def test_product_path_never_touches_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b|liboracle|mx_oracle|oref_", src, flags=re.M), f
+
+
+def test_roof_helpers_validate_before_launch():
+    """The benchmark's measurement helpers (libmxq_roof.so, not part of the
+    C ABI) export their two calls and refuse bad arguments without launching."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "mx9_dual_axis_amd", "libmxq_roof.so"))
+    lib.mxq_roof.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.mxq_roof_cast_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_void_p]
+    assert lib.mxq_roof(0, FAKE, FAKE * 2, 4095, None) == -1          # not a multiple of 4 KiB
+    assert lib.mxq_roof(0, FAKE + 8, FAKE * 2, 4096, None) == -1      # misaligned
+    assert lib.mxq_roof(7, FAKE, FAKE * 2, 4096, None) == -1          # no such kind
+    assert lib.mxq_roof_cast_stream(1, FAKE, None, 100, 128, None) == -1
+    assert lib.mxq_roof_cast_stream(0, FAKE, None, 128, 128, None) == -1   # the read needs a sink
+    assert lib.mxq_roof_cast_stream(3, FAKE, FAKE, 128, 128, None) == -1

@@ -253,9 +253,11 @@ int mx9_unpack_strided(const int8_t *q, int64_t ld_q, const uint8_t *max_exp, in
  *   q, max_exp, prime  as for mx9_pack, nb = outer * inner * nbl blocks.
  *
  * Errors: MX_E_NULL, MX_E_DTYPE, MX_E_BLOCK (block_size != 16), MX_E_SHAPE
- * (a negative or too large dimension), MX_E_ALIGN (x not aligned to its
- * element size, q not 16-byte aligned), MX_E_OVERLAP.  A zero dimension is
- * a no-op.
+ * (a negative or too large dimension, more than 2^32 blocks, or, for
+ * inner > 1, a view whose tiles -- one workgroup of up to 512 threads per
+ * tile of 64 or 128 inner positions -- need a grid beyond 2^32 threads),
+ * MX_E_ALIGN (x not aligned to its element size, q not 16-byte aligned),
+ * MX_E_OVERLAP.  A zero dimension is a no-op.
  */
 int mx9_pack_axis(const void *x, int32_t dtype, int64_t outer, int64_t len, int64_t inner,
                   int32_t block_size, int8_t *q, uint8_t *max_exp, uint8_t *prime, void *stream);

@@ -37,6 +37,8 @@
 //     axis.
 //   * strided (inner == 1): records with a pitch or a ragged row, one thread
 //     per block.
+#include <algorithm>
+
 #include "mxq_kernels.h"
 #include "mx9_codec.h"
 
@@ -65,6 +67,33 @@ __device__ __forceinline__ uint32_t load_bits(const void* xv, uint64_t idx, int 
 // 32.5-32.8 us (bf16); per-wave stages of 4 groups 54.4 us and 30.1 us.
 constexpr int kRecGroups = 4;
 
+// Stage one lane's share of a record as 16-bit LDS writes.  A record starts
+// at an even LDS offset, so its bytes pair up as (exponent, q0), (q1, q2),
+// ..., (q15, prime): pair m holds q[2m - 1] and q[2m].  The lane holding
+// q[e0 .. e0 + kE - 1] (e0 = kE * part) writes pairs kE/2 * part ..
+// kE/2 * (part + 1) - 1, whose first byte is the last q byte of the lane
+// below (the exponent for part 0), and the last lane adds (q15, prime).
+// Measured on MI355X for the [4096, 14336] weights, byte-identical output:
+// 57.3 -> 49.3 us (fp32) and 31.8 -> 31.3 us (bf16) against byte writes.
+template <int kDtype>
+__device__ __forceinline__ void stage_record_piece(uint8_t* rec, const FlatPiece<kDtype>& r, uint32_t part,
+                                                   uint32_t below) {
+    using P = FlatPiece<kDtype>;
+    constexpr int kE = P::kElems;
+    uint16_t* rec16 = reinterpret_cast<uint16_t*>(rec);
+    const uint32_t first = part == 0 ? r.S : below;
+#pragma unroll
+    for (int h = 0; h < kE / 2; ++h) {
+        const uint32_t lo = h == 0 ? first : (r.qd[(2 * h - 1) >> 2] >> (8 * ((2 * h - 1) & 3))) & 0xFFu;
+        const uint32_t hi = (r.qd[(2 * h) >> 2] >> (8 * ((2 * h) & 3))) & 0xFFu;
+        rec16[(kE / 2) * part + h] = uint16_t(lo | (hi << 8));
+    }
+    if (part == P::kLanes - 1) {
+        const uint32_t last = (r.qd[(kE - 1) >> 2] >> (8 * ((kE - 1) & 3))) & 0xFFu;
+        rec16[8] = uint16_t(last | (r.prime << 8));
+    }
+}
+
 template <int kDtype>
 __global__ __launch_bounds__(kThreads)
 void mx9_pack_records_flat(const void* __restrict__ xv, uint64_t nb, uint8_t* __restrict__ packed) {
@@ -90,11 +119,11 @@ void mx9_pack_records_flat(const void* __restrict__ xv, uint64_t nb, uint8_t* __
 #pragma unroll
     for (int k = 0; k < kRecGroups; ++k) {
         const P r = pack_flat_piece<kDtype>(make_uint4(v[k].x, v[k].y, v[k].z, v[k].w), part);
-        uint8_t* rec = st + kRec * (k * kGB + lb);
-        if (part == 0) rec[0] = uint8_t(r.S);
-        if (part == P::kLanes - 1) rec[kRec - 1] = uint8_t(r.prime);
-#pragma unroll
-        for (int e = 0; e < P::kElems; ++e) rec[1 + part * P::kElems + e] = uint8_t(r.qd[e >> 2] >> (8 * (e & 3)));
+        // the last q byte of the lane below (row_shr:1; lanes of a block are
+        // adjacent and a block never spans two rows of 16 lanes)
+        const uint32_t last = (r.qd[(P::kElems - 1) >> 2] >> (8 * ((P::kElems - 1) & 3))) & 0xFFu;
+        const uint32_t below = uint32_t(__builtin_amdgcn_mov_dpp(int(last), 0x111, 0xF, 0xF, false));
+        stage_record_piece<kDtype>(st + kRec * (k * kGB + lb), r, part, below);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);                         // lgkmcnt(0): the wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
@@ -301,12 +330,44 @@ struct TileCoord {
     uint32_t j0, rows, nj;    // rows: live inner positions, nj: live blocks per row
 };
 
+// The pack's order: tile row (o, ti) -- the tiles of one inner range --
+// runs on one XCD, which walks its blocks' tiles tj in turn.  Workgroups are
+// dealt to the 8 XCDs round-robin, so workgroup wg runs on XCD x = wg % 8 and
+// is that XCD's k-th (k = wg / 8); XCD x takes tile rows x, x + 8, x + 16,
+// ...  The max_exp and prime lines of a row (8 tiles' 16-byte pieces) are
+// then completed in one L2 by consecutive tiles, and the 8 XCDs read
+// adjacent column ranges of the same element rows.  Workgroups past the last
+// tile row (when the row count is not a multiple of 8) return at once.
+// Measured on MI355X for [4096, 14336] along axis 0 (byte-identical output):
+// 57.3 -> 51.7 us (fp32) and 37.3 -> 33.8 us (bf16) against the order below.
+template <int kPer, int kTJ = 32>
+__device__ __forceinline__ bool tile_coord_walk(const AxisTiles& v, TileCoord& c) {
+    using T = Tile<kPer, kTJ>;
+    const uint64_t x = blockIdx.x & 7u, k = blockIdx.x >> 3;
+    const uint64_t row = 8 * (k / v.tiles_j) + x;          // tile row: o * tiles_i + ti
+    if (row >= v.outer * v.tiles_i) return false;
+    const uint32_t tj = uint32_t(k % v.tiles_j);
+    const uint32_t ti = uint32_t(row % v.tiles_i);
+    c.o = row / v.tiles_i;
+    c.i0 = uint64_t(ti) * T::kI;
+    c.j0 = tj * T::kJ;
+    c.rows = uint32_t(v.inner - c.i0 < uint64_t(T::kI) ? v.inner - c.i0 : uint64_t(T::kI));
+    c.nj = v.nbl - c.j0 < uint32_t(T::kJ) ? v.nbl - c.j0 : uint32_t(T::kJ);
+    return true;
+}
+
+// Grid of the pack's order: 8 XCDs x ceil(tile rows / 8) x tiles_j.
+inline uint64_t walk_grid(const AxisTiles& v) {
+    return 8 * ((v.outer * v.tiles_i + 7) / 8) * v.tiles_j;
+}
+
 template <int kPer, int kTJ = 32>
 __device__ __forceinline__ TileCoord tile_coord(const AxisTiles& v) {
     using T = Tile<kPer, kTJ>;
     TileCoord c;
-    // consecutive workgroups take consecutive inner ranges of the same
-    // element rows, so the rows' segments are read (and written) together
+    // the unpack's order: consecutive workgroups take consecutive inner
+    // ranges of the same element rows, so the rows' segments are read (and
+    // written) together
     const uint64_t wg = blockIdx.x;
     const uint32_t ti = uint32_t(wg % v.tiles_i);
     const uint64_t rest = wg / v.tiles_i;
@@ -402,7 +463,8 @@ void mx9_pack_axis_tile(const void* __restrict__ xv, AxisTiles v, int8_t* __rest
     using T = Tile<kPer, 32, kPackThreads / 64>;
     __shared__ uint4 lds[T::kLds / 16];
     uint8_t* ls = reinterpret_cast<uint8_t*>(lds);
-    const TileCoord c = tile_coord<kPer>(v);
+    TileCoord c;
+    if (!tile_coord_walk<kPer>(v, c)) return;       // uniform across the workgroup, before any barrier
     const uint32_t il = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t r0 = il * kPer;                  // the lane's first row in the tile
@@ -639,7 +701,7 @@ void launch_pack_tiles(const void* x, int dtype, int64_t outer, int64_t len, int
                        uint8_t* max_exp, uint8_t* prime, uint8_t* packed, int64_t ld_p, hipStream_t stream) {
     const int per = per_lane(inner, x, dtype == 0 ? 4 : 2);
     const AxisTiles v = make_tiles(outer, len, inner, per, 32);
-    const dim3 grid(uint32_t(v.outer * v.tiles_i * v.tiles_j));
+    const dim3 grid(uint32_t(walk_grid(v)));
     const bool vec = aligned16(packed) && ld_p % 16 == 0;
     if (dtype == 0 && per == 2) hipLaunchKernelGGL((mx9_pack_axis_tile<0, kRecords, 2>), grid, dim3(kPackThreads), 0, stream, x, v, q, max_exp, prime, packed, ld_p, vec);
     else if (dtype == 0) hipLaunchKernelGGL((mx9_pack_axis_tile<0, kRecords, 1>), grid, dim3(kPackThreads), 0, stream, x, v, q, max_exp, prime, packed, ld_p, vec);
@@ -677,6 +739,18 @@ void launch_unpack_records_rows(const uint8_t* packed, int64_t ld_p, int64_t row
 }
 
 }  // namespace
+
+uint64_t mx9_axis_grid_threads(int64_t outer, int64_t len, int64_t inner) {
+    uint64_t most = 0;
+    for (int per = 1; per <= 2; ++per) {
+        const uint64_t pack = walk_grid(make_tiles(outer, len, inner, per, 32)) * kPackThreads;
+        const AxisTiles u3 = make_tiles(outer, len, inner, per, kUnpackTJ<false>);
+        const AxisTiles ur = make_tiles(outer, len, inner, per, kUnpackTJ<true>);
+        const uint64_t unpack = std::max(u3.outer * u3.tiles_i * u3.tiles_j, ur.outer * ur.tiles_i * ur.tiles_j) * kThreads;
+        most = std::max(most, std::max(pack, unpack));
+    }
+    return most;
+}
 
 hipError_t launch_mx9_pack_axis(const void* x, int dtype, int64_t outer, int64_t len, int64_t inner,
                                 int8_t* q, uint8_t* max_exp, uint8_t* prime, hipStream_t stream) {

@@ -118,6 +118,8 @@ int check_mx9_view(int32_t dtype, int64_t outer, int64_t len, int64_t inner, int
     if (elems > (uint64_t(1) << 40)) return MX_E_SHAPE;
     *nb = uint64_t(outer) * uint64_t(inner) * uint64_t((len + 15) / 16);
     if (*nb > kMaxThreads) return MX_E_SHAPE;
+    // the tile kernels of a non-last axis: one workgroup per tile
+    if (*nb > 0 && inner > 1 && mxq::mx9_axis_grid_threads(outer, len, inner) > kMaxThreads) return MX_E_SHAPE;
     return MX_OK;
 }
 

@@ -43,6 +43,11 @@ hipError_t launch_mx9_unpack_axis(const int8_t* q, const uint8_t* max_exp, const
                                   int64_t outer, int64_t len, int64_t inner, int out_dtype, void* y,
                                   hipStream_t stream);
 
+// The largest grid, in threads, that the axis and record calls may launch
+// for an [outer, len, inner] view with inner > 1 (tile kernels), over both
+// lane layouts; the caller rejects views whose grid would not fit 32 bits.
+uint64_t mx9_axis_grid_threads(int64_t outer, int64_t len, int64_t inner);
+
 // The same blocks as 18-byte records (exponent byte, q[16], prime byte); the
 // records of one (o, i) form a row, rows at a pitch of ld_p bytes.
 hipError_t launch_mx9_pack_records(const void* x, int dtype, int64_t outer, int64_t len, int64_t inner,

@@ -146,6 +146,10 @@ def test_mx9_axis_and_record_validation_codes():
     assert pack_axis(x=None) == 1 and pack_axis(dtype=2) == 2 and pack_axis(bs=32) == 3
     assert pack_axis(inner=-1) == 5 and pack_axis(length=(1 << 30) + 1) == 5
     assert pack_axis(outer=1 << 20, inner=1 << 20, length=1 << 20) == 5
+    # 2^24 blocks, but 2^23 tiles of one 512-thread workgroup each: the grid would need 2^32 threads
+    assert pack_axis(outer=1 << 23, length=16, inner=2) == 5
+    assert unpack_axis(outer=1 << 23, length=16, inner=2) == 5
+    assert pack_rec(outer=1 << 23, length=16, inner=2, ld=18) == 5
     assert pack_axis(x=FAKE + 1) == 7 and pack_axis(q=FAKE * 2 + 8) == 7
     assert pack_axis(e=FAKE * 2 + 16) == 8                        # max_exp inside q
     assert pack_axis(outer=0, x=None, q=None, e=None, p=None) == 0
@@ -157,8 +161,8 @@ def test_mx9_axis_and_record_validation_codes():
     assert pack_rec(x=FAKE + 2) == 7
     assert pack_rec(pk=FAKE + 64) == 8                            # records inside the input
     assert pack_rec(length=0, x=None, pk=None) == 0
-    assert pack_rec(outer=1 << 20, inner=1 << 11, length=16, ld=1 << 40) == 6
-    assert unpack_rec(outer=1 << 20, inner=1 << 11, length=16, ld=1 << 40) == 6
+    assert pack_rec(outer=1 << 12, inner=1 << 11, length=16, ld=1 << 40) == 6
+    assert unpack_rec(outer=1 << 12, inner=1 << 11, length=16, ld=1 << 40) == 6
     assert unpack_rec(pk=None) == 1 and unpack_rec(od=2) == 2 and unpack_rec(ld=10) == 6
     assert unpack_rec(y=FAKE * 5 + 2) == 7 and unpack_rec(y=FAKE * 2 + 100) == 8
     assert unpack_rec(inner=0, y=None, pk=None) == 0

@@ -18,6 +18,11 @@ Sources (web pages):
   * AMD-AGI/ALTO PR #31 "Add MXFP8 grouped GEMM (E4M3) for routed-expert MoE
     training" -- the contraction that consumes the MXFP8 outputs (description:
     E4M3 operands with block-32 E8M0 scales, 1-D cumulative offsets).
+
+Parity unpinned (oracle-defined): besides the readings listed in
+``mx_oracle.c``, the matrix-core scale layout (``mfma_scale_index``) is this
+project's own; no page fixes it.  It is pinned only by hand-worked positions,
+its bijectivity and the contraction that reads it.
 """
 from __future__ import annotations
 

@@ -17,11 +17,11 @@
 //   * flat records: contiguous input blocks and contiguous records.  The
 //     lanes hold blocks exactly as the flat three-part pack does (a block
 //     over 2 lanes for bf16, 4 for fp32; every wave-wide load is one
-//     contiguous range).  A wave of the pack takes four groups of 32 (bf16)
-//     or 16 (fp32) contiguous blocks and issues all their loads first; its
-//     records are assembled in the wave's own slice of LDS and written as
-//     16-byte chunks, so the 18-byte records cost no unaligned global
-//     stores.  The unpack stages a workgroup's records the same way.
+//     contiguous range).  A wave of the pack takes 64 contiguous blocks (two
+//     groups of 32 for bf16, four of 16 for fp32) and issues all their loads
+//     first; its records are assembled in the wave's own slice of LDS with
+//     16-bit writes and written as 16-byte chunks, so the 18-byte records
+//     cost no unaligned global stores.  The unpack stages a workgroup's records the same way.
 //   * axis tiles (inner > 1): a workgroup takes 64 consecutive inner
 //     positions i of one o and 32 consecutive blocks j (128 and 16 when the
 //     inner extent is even: a lane then takes two adjacent i, so one 32-bit
@@ -60,12 +60,17 @@ __device__ __forceinline__ uint32_t load_bits(const void* xv, uint64_t idx, int 
 // ---------------------------------------------------------------------------
 
 // Groups of 64 / kLanes blocks (one wave-wide 1 KiB load) that one wave of
-// the flat record pack takes.  A wave's blocks are contiguous, so are its
-// records, and it stages them in its own slice of LDS: no workgroup barrier.
-// Measured on MI355X for the [4096, 14336] weights (byte-identical output):
-// one workgroup-wide stage of 8 x 256 lanes' blocks 58-60 us (fp32) and
-// 32.5-32.8 us (bf16); per-wave stages of 4 groups 54.4 us and 30.1 us.
-constexpr int kRecGroups = 4;
+// the flat record pack takes: four for fp32, two for bf16, so that a wave's
+// records are 64 blocks, 1,152 bytes, either way.  A wave's blocks are
+// contiguous, so are its records, and it stages them in its own slice of
+// LDS: no workgroup barrier.  Measured on MI355X for the [4096, 14336]
+// weights (byte-identical output): one workgroup-wide stage of 8 x 256
+// lanes' blocks 58-60 us (fp32) and 32.5-32.8 us (bf16); per-wave stages of
+// 4 groups 54.4 us and 30.1 us; with the 16-bit staging below, 2, 4 and 8
+// groups took 50.2, 49.8 and 50.3-50.9 us (fp32) and 30.5, 31.0-31.1 and
+// 32.0-32.2 us (bf16).
+template <int kDtype>
+constexpr int kRecGroups = kDtype == 0 ? 4 : 2;
 
 // Stage one lane's share of a record as 16-bit LDS writes.  A record starts
 // at an even LDS offset, so its bytes pair up as (exponent, q0), (q1, q2),
@@ -99,8 +104,9 @@ __global__ __launch_bounds__(kThreads)
 void mx9_pack_records_flat(const void* __restrict__ xv, uint64_t nb, uint8_t* __restrict__ packed) {
     using P = FlatPiece<kDtype>;
     constexpr int kGB = 64 / P::kLanes;                          // blocks per group (16 or 32)
-    constexpr int kWB = kRecGroups * kGB;                        // blocks per wave (64 or 128)
-    constexpr int kBytes = kWB * kRec;                           // record bytes per wave (1152 or 2304)
+    constexpr int kG = kRecGroups<kDtype>;
+    constexpr int kWB = kG * kGB;                                // blocks per wave (64)
+    constexpr int kBytes = kWB * kRec;                           // record bytes per wave (1152)
     static_assert(kBytes % 16 == 0, "a wave's records are whole 16-byte chunks");
     __shared__ uint4 stage[kThreads / 64][kBytes / 16];
     typedef unsigned int u4 __attribute__((ext_vector_type(4)));
@@ -110,14 +116,14 @@ void mx9_pack_records_flat(const void* __restrict__ xv, uint64_t nb, uint8_t* __
     if (blk0 >= nb) return;                                      // uniform across the wave
     const uint32_t part = lane % P::kLanes, lb = lane / P::kLanes;
     const u4* src = reinterpret_cast<const u4*>(xv) + blk0 * P::kLanes + lane;
-    u4 v[kRecGroups];
+    u4 v[kG];
 #pragma unroll
-    for (int k = 0; k < kRecGroups; ++k) {
+    for (int k = 0; k < kG; ++k) {
         v[k] = u4{0u, 0u, 0u, 0u};
         if (blk0 + k * kGB + lb < nb) v[k] = __builtin_nontemporal_load(src + k * 64);
     }
 #pragma unroll
-    for (int k = 0; k < kRecGroups; ++k) {
+    for (int k = 0; k < kG; ++k) {
         const P r = pack_flat_piece<kDtype>(make_uint4(v[k].x, v[k].y, v[k].z, v[k].w), part);
         // the last q byte of the lane below (row_shr:1; lanes of a block are
         // adjacent and a block never spans two rows of 16 lanes)
@@ -776,7 +782,7 @@ hipError_t launch_mx9_pack_records(const void* x, int dtype, int64_t outer, int6
     const int64_t nbl = (len + 15) / 16;
     if (inner == 1 && len % 16 == 0 && ld_p == kRec * nbl && aligned16(x) && aligned16(packed)) {
         const uint64_t nb = uint64_t(outer) * uint64_t(nbl);
-        const uint64_t per_wg = uint64_t(kThreads / 64) * kRecGroups * (dtype == 0 ? 16u : 32u);
+        const uint64_t per_wg = uint64_t(kThreads / 64) * 64u;   // 64 blocks per wave, either dtype
         const dim3 grid(uint32_t((nb + per_wg - 1) / per_wg));
         if (dtype == 0) hipLaunchKernelGGL(mx9_pack_records_flat<0>, grid, dim3(kThreads), 0, stream, x, nb, packed);
         else hipLaunchKernelGGL(mx9_pack_records_flat<1>, grid, dim3(kThreads), 0, stream, x, nb, packed);

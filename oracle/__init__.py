@@ -453,7 +453,7 @@ def mx_grouped_gemm_k(A, sA, B, sB, offs, *, sa_strides, sb_strides, threads: in
 
 
 # ---------------------------------------------------------------------------
-# Matrix-core scale layout (a layout of this build for the MXFP8 contraction's
+# Matrix-core scale layout (this project's layout for the MXFP8 contraction's
 # consumer; the pages ask for scales in the consumer's own layout so that no
 # rearrangement runs between the cast and the GEMM)
 # ---------------------------------------------------------------------------

@@ -1,8 +1,8 @@
 """Pins for the matrix-core scale layout (the consumer layout in which the
 cast can emit its E8M0 scales and the MXFP8 contraction reads them; pages:
 pytorch/ao PR #4995, whose kernel emits the consumer's scale layout directly
-so that no rearrangement runs in between).  The layout itself is defined by
-this build; these tests pin that the oracle's index function is a bijection
+so that no rearrangement runs in between).  The layout itself is this
+project's own; these tests pin that the oracle's index function is a bijection
 with the stated lane and byte assignment, worked by hand."""
 import numpy as np
 import pytest

@@ -14,7 +14,7 @@ launch stream (the call is one kernel), against MI355X's 8 TB/s HBM peak.
 ``traffic`` is the HBM byte count per call from the committed rocprofv3
 FETCH_SIZE / WRITE_SIZE summary, reported only while the kernel source
 matches the source those counters were taken on.  ``box_roofs`` gives, for
-context, what the same box reaches for a plain copy, read and write of the
+context, what the same GPU reaches for a plain copy, read and write of the
 cast's byte volume with hand-written streaming kernels, and
 ``roofline.frac_of_box_copy`` the cast's rate against that copy.
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
@@ -81,7 +81,7 @@ def committed_traffic():
 
 
 def box_roofs(dev, volume: int, launches: int = 10):
-    """What this box achieves for plain streams of `volume` bytes: a copy
+    """What this GPU achieves for plain streams of `volume` bytes: a copy
     (half the volume read, half written), a read and a write, each by the
     hand-written kernels of libmxq_roof.so (one 16-byte non-temporal access
     per lane, 4 KiB per workgroup), alternating two buffers of `volume` bytes
@@ -608,7 +608,7 @@ def main():
     torch.cuda.synchronize()
     stream_gbs = 2 * half * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst, src32, dst32
-    # and by the hand-written streams: this box's own roof for the cast's volume
+    # and by the hand-written streams: this GPU's own roof for the cast's volume
     roofs = box_roofs(dev, int(kbytes["dual_axis"]))
 
     # context: the dual-axis cast alone on the same matrix, back-to-back calls

@@ -2,7 +2,7 @@
 // quantization path and not part of libmxq.so's C ABI).
 //
 // The benchmark reports the dual-axis cast against MI355X's published HBM
-// peak and, for context, against what the same box achieves for a plain
+// peak and, for context, against what the same GPU achieves for a plain
 // stream of the same byte volume.  These kernels are those streams, written
 // for the access pattern that measured fastest on MI355X: each workgroup
 // (4 waves) moves one 4 KiB chunk with one 16-byte non-temporal load and/or

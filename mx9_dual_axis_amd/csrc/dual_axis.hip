@@ -17,10 +17,12 @@
 //              per-element test.  The cast runs from registers.
 //   * LDS    : the tile is written once (32 KiB).  The 16-byte chunk index of
 //              each row is XORed with a function of the row's 16-row chunk c
-//              (2c + c/4, lds_chunk_xor), so that the 32 lanes of each half of
-//              a colwise dword read (8 chunks x 4 column pairs) hit 32
-//              distinct banks: SQ_LDS_BANK_CONFLICT reads 0 (with 2c alone,
-//              a two-way conflict, 31% of the LDS-active cycles).
+//              (2c + c/4, lds_chunk_xor), so that the lanes of a colwise
+//              dword read (8 chunks x 8 column pairs per wave) hit distinct
+//              banks (with 2c alone, a two-way conflict took 31% of the
+//              LDS-active cycles).  What conflicts remain (7% of the
+//              LDS-active cycles of a stress call) come from the small scale
+//              stagings; the kernel is bound by memory, not by LDS.
 //   * colwise: a unit is (column pair, 16-row chunk); each thread takes one.
 //              A packed u16 max over 16 LDS dwords plus one DPP step between
 //              the two chunks of a 32-row block gives both column maxima;

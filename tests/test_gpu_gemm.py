@@ -161,6 +161,95 @@ def test_row_groups_every_tile_once(M, covered):
     assert torch.all(out[covered:] == 0)
 
 
+def _clamped_ends(offs, hi):
+    """The group ends the pipelined kernels read from any offsets: each
+    rounded toward zero to a multiple of 128, clamped to [0, hi], then a
+    running maximum.  The header leaves the expert of rows under invalid
+    offsets unspecified; the kernels take this reading, under which the
+    row tiles still partition the rows."""
+    ends, c = [], 0
+    for o in offs:
+        v = int(o / 128) * 128
+        c = max(c, min(max(v, 0), hi))
+        ends.append(c)
+    return np.array(ends, np.int32)
+
+
+@pytest.mark.parametrize("offs", [[640, 128, 5000, 300], [-300, 256, 200, 768], [1100, 0, 0, 0], [200, 330, 900, 1000]])
+def test_row_groups_invalid_offsets(offs):
+    """Offsets that are unsorted, negative, past M or not multiples of 128:
+    the forward stays inside its operands, writes every output row once, and
+    gives what valid offsets at the clamped ends give (both scale forms of
+    the pipelined kernel)."""
+    require_gpu()
+    say(f"mx_grouped_gemm_rows invalid offs {offs}")
+    g = np.random.default_rng(sum(abs(o) for o in offs))
+    M, N, K, E = 1024, 384, 256, 4
+    A = _codes(g, (M, K))
+    sA = g.integers(118, 137, (M, K // 32), dtype=np.uint8)
+    B = np.stack([_codes(g, (N, K)) for _ in range(E)])
+    sB = g.integers(118, 137, (E, N, K // 32), dtype=np.uint8)
+    o = np.array(offs, np.int32)
+    ends = _clamped_ends(offs, M)
+    ref, absC = oracle.mx_grouped_gemm_rows(A, sA, B, sB, ends, sa_strides=(K // 32, 1), sb_strides=(K // 32, 1),
+                                            threads=THREADS, with_abs=True)
+    outs = {}
+    for form in ("rows", "mfma"):
+        out = torch.full((M, N), 3.0, dtype=torch.float32, device=DEV)
+        if form == "rows":
+            mxq.mx_grouped_gemm_rows(_dev(A), _dev(sA), _dev(B), _dev(sB), _dev(o), out=out)
+        else:
+            sBm = np.stack([oracle.scales_to_mfma(sB[e]) for e in range(E)])
+            mxq.mx_grouped_gemm_rows_mfma(_dev(A), _dev(oracle.scales_to_mfma(sA)), _dev(B), _dev(sBm), _dev(o),
+                                          out=out)
+        torch.cuda.synchronize()
+        _assert_close(out, ref, absC, K, torch.float32, f"invalid offs {offs} ({form})")
+        assert torch.all(out[int(ends[-1]):] == 0)
+        outs[form] = out
+    assert torch.equal(outs["rows"], outs["mfma"])
+
+
+def _clamp_range(lo_raw, hi_raw, K):
+    """The contraction range [k_lo, k_hi) the pipelined kernel reads for one
+    group from its two raw offsets: k_lo is the previous offset clamped to
+    [0, K], k_hi the group's clamped to [k_lo, K], both rounded down to a
+    multiple of 128 from 0 and from k_lo."""
+    lo = min(max(lo_raw, 0), K)
+    lo -= lo % 128
+    hi = min(max(hi_raw, lo), K)
+    hi -= (hi - lo) % 128
+    return lo, hi
+
+
+@pytest.mark.parametrize("offs", [[300, 100, 900, 5000], [-128, 640, 512, 1024]])
+def test_contraction_groups_invalid_offsets(offs):
+    """The weight gradient under invalid offsets: each group's range is its
+    two offsets clamped to multiples of 128 inside [0, K] (ranges may then
+    overlap or be empty); every access stays inside the operands and each
+    group's result is the contraction over its clamped range."""
+    require_gpu()
+    say(f"mx_grouped_gemm_k invalid offs {offs}")
+    g = np.random.default_rng(7 + sum(abs(o) for o in offs))
+    M, N, K = 256, 384, 1024
+    A, B = _codes(g, (M, K)), _codes(g, (N, K))
+    sAc = g.integers(118, 137, (K // 32, M), dtype=np.uint8)
+    sBc = g.integers(118, 137, (K // 32, N), dtype=np.uint8)
+    C = mxq.mx_grouped_gemm_k(_dev(A), _dev(sAc).t(), _dev(B), _dev(sBc).t(), _dev(np.array(offs, np.int32)))
+    torch.cuda.synchronize()
+    prev = 0
+    for e, raw in enumerate(offs):
+        lo, hi = _clamp_range(prev, raw, K)
+        prev = raw
+        if hi == lo:
+            assert torch.all(C[e] == 0), f"group {e} over an empty range"
+            continue
+        ref, absC = oracle.mx_grouped_gemm_k(np.ascontiguousarray(A[:, lo:hi]), sAc[lo // 32:hi // 32],
+                                             np.ascontiguousarray(B[:, lo:hi]), sBc[lo // 32:hi // 32],
+                                             np.array([hi - lo], np.int32), sa_strides=(1, M), sb_strides=(1, N),
+                                             threads=THREADS, with_abs=True)
+        _assert_close(C[e], ref[0], absC[0], hi - lo, torch.float32, f"group {e} [{lo}, {hi})")
+
+
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_contraction_groups_parity(out_dtype):
     require_gpu()

@@ -96,6 +96,54 @@ def test_dense_parity(M, N, K, out_dtype):
     _assert_close(C, ref, absC, K, out_dtype, f"dense {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("K", [512, 2048])
+def test_rows_form_four_step_scale_loads(K):
+    """Rows-form scales whose rows are 16-byte aligned, with K a multiple of
+    512, are loaded four contraction steps at a time (one 16-byte piece per
+    row into a period buffer).  The same scales at a row pitch that is a
+    multiple of 4 only take the per-step route: both give the same bits, and
+    both match the oracle, for the dense product (ragged column tiles) and
+    the row-grouped forward (groups of odd and even unit counts, a tail)."""
+    require_gpu()
+    say(f"rows-form scales in four-step periods, K={K}")
+    g = np.random.default_rng(K + 17)
+    kb = K // 32
+
+    def pitched(S, pad):
+        buf = np.zeros(S.shape[:-1] + (kb + pad,), np.uint8)
+        buf[..., :kb] = S
+        return torch.from_numpy(buf).to(DEV)[..., :kb]
+
+    M, N = 384, 640
+    A, B = _codes(g, (M, K)), _codes(g, (N, K))
+    sA = g.integers(118, 137, (M, kb), dtype=np.uint8)
+    sB = g.integers(118, 137, (N, kb), dtype=np.uint8)
+    ref, absC = oracle.mx_gemm_nt(A, sA, B, sB, sa_strides=(kb, 1), sb_strides=(kb, 1), threads=THREADS,
+                                  with_abs=True)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        C4 = mxq.mx_gemm_nt(_dev(A), pitched(sA, 16), _dev(B), pitched(sB, 16), out_dtype=out_dtype)
+        C1 = mxq.mx_gemm_nt(_dev(A), pitched(sA, 4), _dev(B), pitched(sB, 4), out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(C4.view(torch.int16) if out_dtype == torch.bfloat16 else C4.view(torch.int32),
+                           C1.view(torch.int16) if out_dtype == torch.bfloat16 else C1.view(torch.int32))
+        _assert_close(C4, ref, absC, K, out_dtype, f"dense rows-form periods K={K}")
+
+    M, N, E = 1280, 384, 5
+    A = _codes(g, (M, K))
+    Bs = np.stack([_codes(g, (N, K)) for _ in range(E)])
+    sA = g.integers(118, 137, (M, kb), dtype=np.uint8)
+    sB = g.integers(118, 137, (E, N, kb), dtype=np.uint8)
+    offs = np.array([384, 384, 640, 1024, 1152], np.int32)          # 3, 0, 2, 3, 1 units, a 128-row tail
+    ref, absC = oracle.mx_grouped_gemm_rows(A, sA, Bs, sB, offs, sa_strides=(kb, 1), sb_strides=(kb, 1),
+                                            threads=THREADS, with_abs=True)
+    C4 = mxq.mx_grouped_gemm_rows(_dev(A), _dev(sA), _dev(Bs), _dev(sB), _dev(offs))
+    C1 = mxq.mx_grouped_gemm_rows(_dev(A), pitched(sA, 4), _dev(Bs), pitched(sB, 4), _dev(offs))
+    torch.cuda.synchronize()
+    assert torch.equal(C4.view(torch.int32), C1.view(torch.int32))
+    _assert_close(C4, ref, absC, K, torch.float32, f"row groups rows-form periods K={K}")
+    assert torch.all(C4[offs[-1]:] == 0)
+
+
 def test_dense_transposed_scales_and_pitches():
     """Scales read through transposed views (the colwise cast's s_col layout),
     operand row pitches above K and an output pitch above N."""

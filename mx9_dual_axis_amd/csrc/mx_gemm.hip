@@ -269,7 +269,8 @@ void mx_gemm_kernel(GemmArgs p) {
 // of its own (two buffers, one period ahead).  A per-step dword per row
 // touches one cache line per row and step; measured on MI355X, the
 // row-grouped forward spends a quarter of its time on those requests
-// (234 us against 174-180 us with the same number of contiguous loads).
+// (234 us against 174-180 us with the same number of contiguous loads);
+// in four-step periods it takes 184-189 us, with byte-identical results.
 constexpr int kScalesMfma = 0, kScalesRows = 1, kScalesBlocks = 2, kScalesRows4 = 3;
 
 // A plain run's contribution to a lane's scale dword: byte q of the dword is

@@ -21,8 +21,9 @@
 // takes the matrix-core scale layout, or plain scales whose blocks of a row
 // are adjacent (the rowwise cast's s_row) or whose rows of a block are
 // adjacent (the colwise cast's s_col read through its transpose), with both
-// operands in one form and C rows in 16-byte pieces.  mx_gemm_kernel (below)
-// takes any strided scale views and any C pitch.
+// operands in one form and C rows in 16-byte pieces (rows-form scales with
+// 16-byte aligned rows are loaded four steps at a time).  mx_gemm_kernel
+// (below) takes any strided scale views and any C pitch.
 //
 // mx_gemm_kernel: one workgroup (4 wave64s) per 128 x 128 tile of C; wave w
 // computes the 64 x 64 quarter (w / 2, w % 2) as 4 x 4 instructions per

@@ -14,6 +14,10 @@ element must satisfy
     |C_gpu - C_exact| <= (2^-10 + (K + 2) 2^-24) sum_k |a_k b_k|
 (largest observed: 2^-11.8), with C_exact and the sum of magnitudes from the
 oracle (binary64).  A bf16 output adds its own rounding, 2^-8 |C_exact|.
+The bound still catches a wrong operand, scale or range: one misplaced
+scale byte doubles or halves a 32-block's share of the sum, about 1/(K/32)
+of sum |a_k b_k| (at least 2^-8 for K <= 8192), and a wrong group or row
+moves an element by the order of the sum itself.
 Operands whose products share a narrow exponent range, with scales constant
 along the contraction, add exactly in that tree and in fp32; for them the
 result must equal the oracle's exactly (test_exact_when_no_bits_are_lost).
@@ -78,6 +82,47 @@ def test_exact_when_no_bits_are_lost(M, N, K):
     ref = oracle.mx_gemm_nt(A, sA, B, sB, sa_strides=(K // 32, 1), sb_strides=(K // 32, 1), threads=THREADS)
     got = host(C).astype(np.float64)
     assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} entries differ"
+
+
+def _narrow(g, shape):
+    """E4M3 codes with exponent fields 6..8 (|value| 0.25 .. 3.75), either sign."""
+    e = g.integers(6, 9, shape)
+    return ((g.integers(0, 2, shape) << 7) | (e << 3) | g.integers(0, 8, shape)).astype(np.uint8)
+
+
+def test_exact_grouped_forms():
+    """The exact class of test_exact_when_no_bits_are_lost for both grouped
+    forms: the row-grouped forward (per-row and per-expert scales constant
+    along the contraction, four-step scale periods) and the contraction-
+    grouped weight gradient (scales read through the colwise transpose).
+    Their results must equal the oracle's bit for bit, which pins each
+    group's operand, scale and range selection exactly."""
+    require_gpu()
+    say("grouped forms, exact class")
+    g = np.random.default_rng(99)
+    M, N, K, E = 768, 256, 1024, 4
+    A = _narrow(g, (M, K))
+    Bs = np.stack([_narrow(g, (N, K)) for _ in range(E)])
+    sA = np.repeat(g.integers(120, 134, (M, 1), dtype=np.uint8), K // 32, axis=1)
+    sB = np.repeat(g.integers(120, 134, (E, N, 1), dtype=np.uint8), K // 32, axis=2)
+    offs = np.array([256, 256, 640, 768], np.int32)
+    C = mxq.mx_grouped_gemm_rows(_dev(A), _dev(sA), _dev(Bs), _dev(sB), _dev(offs))
+    torch.cuda.synchronize()
+    ref = oracle.mx_grouped_gemm_rows(A, sA, Bs, sB, offs, sa_strides=(K // 32, 1), sb_strides=(K // 32, 1),
+                                      threads=THREADS)
+    got = host(C).astype(np.float64)
+    assert np.array_equal(got, ref), f"row groups: {np.count_nonzero(got != ref)} entries differ"
+
+    M, N, K = 256, 384, 1024
+    A, B = _narrow(g, (M, K)), _narrow(g, (N, K))
+    sAc = np.repeat(g.integers(120, 134, (1, M), dtype=np.uint8), K // 32, axis=0)      # [K/32, M]
+    sBc = np.repeat(g.integers(120, 134, (1, N), dtype=np.uint8), K // 32, axis=0)
+    offs = np.array([256, 256, 640, 896], np.int32)
+    C = mxq.mx_grouped_gemm_k(_dev(A), _dev(sAc).t(), _dev(B), _dev(sBc).t(), _dev(offs))
+    torch.cuda.synchronize()
+    ref = oracle.mx_grouped_gemm_k(A, sAc, B, sBc, offs, sa_strides=(1, M), sb_strides=(1, N), threads=THREADS)
+    got = host(C).astype(np.float64)
+    assert np.array_equal(got, ref), f"contraction groups: {np.count_nonzero(got != ref)} entries differ"
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])

@@ -328,7 +328,10 @@ int mx9_unpack_records(const uint8_t *packed, int64_t ld_p, int64_t outer, int64
  * multiple of 4, or both have row stride 1 and a block stride that is a
  * multiple of 4 (the cast's s_row and s_col as above), the scale pointers
  * are 4-byte aligned and C rows are whole 16-byte pieces; other views take
- * a slower general kernel with the same results.
+ * a slower general kernel with the same results.  Block-stride-1 scales
+ * whose pointers and row strides are multiples of 16 bytes, with K a
+ * multiple of 512, load faster (four contraction steps per request) in
+ * this call and the row-grouped forward.
  *
  * Errors: MX_E_NULL, MX_E_DTYPE (out_dtype), MX_E_SHAPE (also when a kernel's
  * grid would exceed 2^32 threads), MX_E_STRIDE (a pitch

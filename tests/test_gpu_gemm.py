@@ -125,6 +125,73 @@ def test_exact_grouped_forms():
     assert np.array_equal(got, ref), f"contraction groups: {np.count_nonzero(got != ref)} entries differ"
 
 
+def _one_hot_blocks(g, rows, K):
+    """E4M3 codes that are 0 except at the first position of every 32-block,
+    where they are +-1 or +-2: each 32-block then contributes one product."""
+    c = np.zeros((rows, K), np.uint8)
+    c[:, ::32] = g.choice(np.array([0x38, 0xB8, 0x40, 0xC0], np.uint8), (rows, K // 32))
+    return c
+
+
+def test_exact_one_hot_blocks_every_scale_layout():
+    """Scales that differ in every row and every 32-block (exponents 125..129)
+    with one nonzero product per block: every block's term is exact and the
+    terms span few enough bits that fp32 sums them exactly, so each result
+    must equal the oracle's bit for bit.  A scale read from the wrong row or
+    block changes the result, so this pins, through the matrix instruction
+    itself, the matrix-core scale layout (scales_to_mfma) and the plain
+    forms, for the dense product and both grouped forms."""
+    require_gpu()
+    say("one-hot blocks, every scale layout, exact")
+    g = np.random.default_rng(123)
+    M, N, K, E = 512, 256, 1024, 3
+    kb = K // 32
+    A, B = _one_hot_blocks(g, M, K), _one_hot_blocks(g, N, K)
+    sA = g.integers(125, 130, (M, kb), dtype=np.uint8)
+    sB = g.integers(125, 130, (N, kb), dtype=np.uint8)
+    ref = oracle.mx_gemm_nt(A, sA, B, sB, sa_strides=(kb, 1), sb_strides=(kb, 1), threads=THREADS)
+    for form in ("mfma", "rows", "blocks"):
+        if form == "mfma":
+            C = mxq.mx_gemm_nt_mfma(_dev(A), _dev(oracle.scales_to_mfma(sA)), _dev(B), _dev(oracle.scales_to_mfma(sB)))
+        elif form == "rows":
+            C = mxq.mx_gemm_nt(_dev(A), _dev(sA), _dev(B), _dev(sB))
+        else:
+            C = mxq.mx_gemm_nt(_dev(A), _dev(np.ascontiguousarray(sA.T)).t(), _dev(B),
+                               _dev(np.ascontiguousarray(sB.T)).t())
+        torch.cuda.synchronize()
+        got = host(C).astype(np.float64)
+        assert np.array_equal(got, ref), f"dense ({form}): {np.count_nonzero(got != ref)} entries differ"
+
+    Bs = np.stack([_one_hot_blocks(g, N, K) for _ in range(E)])
+    sBs = g.integers(125, 130, (E, N, kb), dtype=np.uint8)
+    offs = np.array([128, 384, 384], np.int32)
+    ref = oracle.mx_grouped_gemm_rows(A, sA, Bs, sBs, offs, sa_strides=(kb, 1), sb_strides=(kb, 1), threads=THREADS)
+    sBm = np.stack([oracle.scales_to_mfma(sBs[e]) for e in range(E)])
+    for form in ("mfma", "rows"):
+        if form == "mfma":
+            C = mxq.mx_grouped_gemm_rows_mfma(_dev(A), _dev(oracle.scales_to_mfma(sA)), _dev(Bs), _dev(sBm),
+                                              _dev(offs))
+        else:
+            C = mxq.mx_grouped_gemm_rows(_dev(A), _dev(sA), _dev(Bs), _dev(sBs), _dev(offs))
+        torch.cuda.synchronize()
+        got = host(C).astype(np.float64)
+        assert np.array_equal(got, ref), f"row groups ({form}): {np.count_nonzero(got != ref)} entries differ"
+
+    # contraction groups: A [M, K] and B [N, K] with the 32-blocks along the tokens
+    offs = np.array([256, 256, 768, 896], np.int32)
+    sAc, sBc = np.ascontiguousarray(sA.T), np.ascontiguousarray(sB.T)              # [K/32, M], [K/32, N]
+    ref = oracle.mx_grouped_gemm_k(A, sAc, B, sBc, offs, sa_strides=(1, M), sb_strides=(1, N), threads=THREADS)
+    for form in ("mfma", "blocks"):
+        if form == "mfma":
+            C = mxq.mx_grouped_gemm_k_mfma(_dev(A), _dev(oracle.scales_to_mfma(sA)), _dev(B),
+                                           _dev(oracle.scales_to_mfma(sB)), _dev(offs))
+        else:
+            C = mxq.mx_grouped_gemm_k(_dev(A), _dev(sAc).t(), _dev(B), _dev(sBc).t(), _dev(offs))
+        torch.cuda.synchronize()
+        got = host(C).astype(np.float64)
+        assert np.array_equal(got, ref), f"contraction groups ({form}): {np.count_nonzero(got != ref)} entries differ"
+
+
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("M,N,K", [(128, 128, 128), (256, 384, 512), (384, 256, 1024)])
 def test_dense_parity(M, N, K, out_dtype):

@@ -19,10 +19,13 @@ Sources (web pages):
     training" -- the contraction that consumes the MXFP8 outputs (description:
     E4M3 operands with block-32 E8M0 scales, 1-D cumulative offsets).
 
-Parity unpinned (oracle-defined): besides the readings listed in
-``mx_oracle.c``, the matrix-core scale layout (``mfma_scale_index``) is this
-project's own; no page fixes it.  It is pinned only by hand-worked positions,
-its bijectivity and the contraction that reads it.
+The matrix-core scale layout (``mfma_scale_index``) is this project's own;
+no page fixes it.  It is pinned by hand-worked positions, its bijectivity,
+and the matrix instruction that consumes it: contractions whose scales
+differ in every row and 32-block, with one product per block, must equal
+this oracle's plain-scale result bit for bit when their scales go through
+``scales_to_mfma`` (the GPU tests of the contraction).  The readings the
+pages leave open are listed, with their pins, in ``mx_oracle.c``.
 """
 from __future__ import annotations
 

@@ -4,7 +4,8 @@ on the given stream).  Each captured call is replayed several times, with
 the outputs overwritten and the device synchronized in between, and every
 replay must reproduce the oracle's bytes (casts, MX9) or the eager result
 bit for bit (contractions, whose eager result is checked against the oracle
-elsewhere)."""
+elsewhere).  Calls issued on two streams, whose kernels may overlap, give
+the bytes of the same calls made one after another."""
 import numpy as np
 import pytest
 import torch
@@ -117,3 +118,38 @@ def test_matrix_core_cast_and_contractions_in_a_graph():
         for a, b in zip((*cast, Y, dW, D), want):
             assert torch.equal(a, b), rep
     _replay(graph, (*cast, Y, dW, D), check)
+
+
+def test_concurrent_calls_on_two_streams():
+    """The library holds no state between calls: the cast, the MX9 pack and
+    unpack and a contraction issued alternately on two streams (so that their
+    kernels may run at the same time) give the same bytes as the same calls
+    made one after another on the default stream."""
+    require_gpu()
+    say("concurrent calls on two streams")
+    g = np.random.default_rng(77)
+    M, N = 1024, 2048
+    xs = [bf16_to_dev(synth.special_matrix(M, N, 40 + i)) for i in range(2)]
+    ws = [torch.from_numpy(synth.mx9_weights(512, 1000, 50 + i, "fp32")).to(DEV) for i in range(2)]
+    As = [_codes(g, (512, 1024)) for _ in range(2)]
+    sAs = [torch.from_numpy(g.integers(118, 137, (512, 32), dtype=np.uint8)).to(DEV) for _ in range(2)]
+
+    def work(i):
+        cast = mxq.mx_quantize_2d_dual(xs[i])
+        q, e, p = mxq.mx9_pack(ws[i])
+        y = mxq.mx9_unpack(q, e, p, ws[i].shape[0], ws[i].shape[1], out_dtype=torch.bfloat16)
+        c = mxq.mx_gemm_nt(As[i], sAs[i], As[1 - i], sAs[1 - i])
+        return list(cast) + [q, e, p, y, c]
+
+    want = [work(i) for i in range(2)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        got = [None, None]
+        for i in (0, 1):
+            with torch.cuda.stream(streams[i]):
+                got[i] = work(i)
+        torch.cuda.synchronize()
+        for i in (0, 1):
+            for k, (a, b) in enumerate(zip(got[i], want[i])):
+                assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"rep {rep} stream {i} output {k}"

@@ -13,10 +13,10 @@ algorithmic bytes per call over its average call time from HIP events on the
 launch stream (the call is one kernel), against MI355X's 8 TB/s HBM peak.
 ``traffic`` is the HBM byte count per call from the committed rocprofv3
 FETCH_SIZE / WRITE_SIZE summary, reported only while the kernel source
-matches the source those counters were taken on.  ``box_roofs`` gives, for
+matches the source those counters were taken on.  ``gpu_roofs`` gives, for
 context, what the same GPU reaches for a plain copy, read and write of the
 cast's byte volume with hand-written streaming kernels, and
-``roofline.frac_of_box_copy`` the cast's rate against that copy.
+``roofline.frac_of_gpu_copy`` the cast's rate against that copy.
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
 workload (a multithreaded leg of about ten seconds and a single-thread leg).
 
@@ -80,7 +80,7 @@ def committed_traffic():
     return float(m_b.group(1))
 
 
-def box_roofs(dev, volume: int, launches: int = 10):
+def gpu_roofs(dev, volume: int, launches: int = 10):
     """What this GPU achieves for plain streams of `volume` bytes: a copy
     (half the volume read, half written), a read and a write, each by the
     hand-written kernels of libmxq_roof.so (one 16-byte non-temporal access
@@ -609,7 +609,7 @@ def main():
     stream_gbs = 2 * half * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst, src32, dst32
     # and by the hand-written streams: this GPU's own roof for the cast's volume
-    roofs = box_roofs(dev, int(kbytes["dual_axis"]))
+    roofs = gpu_roofs(dev, int(kbytes["dual_axis"]))
 
     # context: the dual-axis cast alone on the same matrix, back-to-back calls
     # alternating two output sets (the 1.09 GB per call exceeds the 256 MB
@@ -648,11 +648,11 @@ def main():
                      "launches_timed": len(dual_times),
                      "timed_every_nth_step": EVENT_EVERY,
                      "bracketed_steps": bracketed,
-                     "frac_of_box_copy": round(dual["GB_s"] / roofs["copy_GB_s"], 4)},
+                     "frac_of_gpu_copy": round(dual["GB_s"] / roofs["copy_GB_s"], 4)},
         "kernels": kernels,
         "copy_GB_s": round(copy_gbs, 1),
         "stream_copy_GB_s": round(stream_gbs, 1),
-        "box_roofs": roofs,
+        "gpu_roofs": roofs,
         "kernel_source_sha256_16": source_digest(),
     }
     del x, dual_out, mx9_out, y
